@@ -1,0 +1,31 @@
+"""CPU oracle for the fused attention forward pass.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline leg
+may import anything from this package; the product path (the HIP library and its Python binding)
+never does, and the two share no code.
+
+Everything here is plain float64 NumPy (or pure Python for the tiny brute-force case) written from
+the five pages on tiled/online-softmax attention:
+  * "SDPA and FlashAttention's tiling" (octlm notes),
+  * "Explain tiled attention and verify its output" (aiml.sh lab),
+  * "4.2 FlashAttention I: IO-Awareness & The Online Softmax" (LLM stack book),
+  * "Attention from scratch + roofline" (LLM systems cookbook),
+  * "Efficient attention & KV cache" (ML interview book).
+
+Parity status: every function below is pinned by `tests/test_oracle_pins.py` and
+`tests/test_accounting.py` against values the pages print, closed forms, invariants and library
+special cases. No function is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    brute_attention,
+    dense_attention,
+    dense_head,
+    merge_partials,
+    online_logsumexp_trace,
+    online_softmax,
+    online_softmax_weighted_sum,
+    tiled_attention,
+    tiled_head,
+)
+from . import accounting  # noqa: F401

@@ -1,0 +1,75 @@
+"""Pins of the oracle's accounting to the numbers the pages print (CPU only)."""
+
+import json
+import os
+
+import pytest
+
+from oracle import accounting as acc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_logical_access_sweep_reproduces_the_lab():
+    g = _golden("lab_recorded_result.json")
+    p = g["sweep_model_parameters"]
+    for rec in g["hbm_traffic_sweep"]:
+        got = acc.logical_access_model(rec["seq_len"], rec["num_heads"], rec["head_dim"],
+                                       p["bytes_per_elem"], p["block_q"])
+        for key, val in got.items():
+            assert val == rec[key], key
+
+
+def test_access_count_exceeds_compulsory_and_grows_superlinearly():
+    g = _golden("lab_checks.json")["access_count"]
+    small = acc.logical_access_model(g["small_seq_len"])
+    large = acc.logical_access_model(g["large_seq_len"])
+    assert small["tiled_logical_access_mb_no_cache_reuse"] > small["qkvo_compulsory_bytes_mb"]
+    ratio = (large["tiled_logical_access_mb_no_cache_reuse"]
+             / small["tiled_logical_access_mb_no_cache_reuse"])
+    assert ratio > g["large_over_small_ratio_above"]
+
+
+def test_memory_exercise():
+    g = _golden("memory_exercise.json")
+    a = g["answers_worked_by_hand"]
+    s = acc.score_matrix_bytes(g["N"], g["dtype_bytes"])
+    o = acc.saved_output_bytes(g["N"], g["d"], g["dtype_bytes"], g["lse_bytes"])
+    assert s == a["score_matrix_bytes"]
+    assert o == a["o_plus_l_bytes"]
+    assert round(s / o, 2) == a["ratio"]
+    assert g["M_elements"] // g["d"] ** 2 == a["reduction_factor_M_over_d2"]
+
+
+def test_notebook_intensity_checks():
+    # "Attention from scratch + roofline": AI doubles with T; prefill above the quoted ridges,
+    # decode below 20 FLOP/byte
+    r = acc.arithmetic_intensity(1, 32, 2048, 128) / acc.arithmetic_intensity(1, 32, 1024, 128)
+    assert 1.8 <= r <= 2.2
+    assert acc.arithmetic_intensity(1, 32, 1024, 128) > 203
+    assert acc.decode_intensity(1, 8, 8, 128, 2048) < 20
+    # exercise 1: with a quarter of the kv heads decode intensity rises about fourfold
+    mha = acc.decode_intensity(1, 32, 32, 128, 8192)
+    gqa = acc.decode_intensity(1, 32, 8, 128, 8192)
+    assert gqa / mha == pytest.approx(4.0, rel=1e-3)
+
+
+def test_causal_halving_convention_against_exact_pair_count():
+    exact = acc.attention_flops_exact(1, 32, 8192, 8192, 128, True)
+    halved = acc.attention_flops(1, 32, 8192, 8192, 128, True)
+    assert exact / halved == pytest.approx(1 + 1 / 8192, rel=1e-12)
+    assert acc.visible_pairs(4, 4, True) == 10
+    assert acc.visible_pairs(1, 9, True) == 9
+    assert acc.visible_pairs(3, 5, True) == 3 + 4 + 5
+
+
+def test_decode_bytes_of_gqa_step():
+    # K and V of 64 x 8 heads x 8192 keys x 128 dims in bf16 dominate: 2.1475 GB
+    b = acc.decode_bytes(64, 64, 8, 8192, 128)
+    assert b == 2 * 64 * 8 * 8192 * 128 * 2 + 2 * 64 * 64 * 128 * 2 + 4 * 64 * 64
+    assert round(b / 1e9, 4) == 2.1496
