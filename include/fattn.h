@@ -1,0 +1,120 @@
+/*
+ * libfattn: fused attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * Computes, for every batch b, query head h and query row i,
+ *   O[b,h,i,:] = softmax_j(scale * Q[b,h,i,:] . K[b,g,j,:] + mask(i,j)) V[b,g,j,:]
+ *   LSE[b,h,i] = log sum_j exp(scale * Q[b,h,i,:] . K[b,g,j,:] + mask(i,j))
+ * with g = h / (Hq / Hkv), one query tile at a time: key/value tiles stream through on-chip
+ * memory while a running row maximum, a running sum and an unnormalised accumulator are kept and
+ * rescaled whenever the maximum grows; the Tq x Tk score matrix never reaches device memory.
+ *
+ * Sources of the definition: the online-softmax update and tiled forward of
+ * "4.2 FlashAttention I: IO-Awareness & The Online Softmax" (sections "The key idea: a running
+ * max and a correction factor" and "FlashAttention forward: tiling + online softmax fused into
+ * one pass"), the blockwise forward returning (out, lse) of "Efficient attention & KV cache"
+ * (section 3), and the argument set of the fused attention call on "SDPA and FlashAttention's
+ * tiling" (section "The tiled sketch, in Python": is_causal, scale, enable_gqa).
+ *
+ * Plain C ABI: no HIP or torch types appear here. All entry points are thread-safe.
+ */
+#ifndef FATTN_H
+#define FATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define FATTN_OK 0
+#define FATTN_ERR_INVALID (-1)     /* an argument is out of its documented range */
+#define FATTN_ERR_UNSUPPORTED (-2) /* valid but not implemented (head dim not 32, 64 or 128) */
+#define FATTN_ERR_HIP (-3)         /* the HIP runtime reported an error at launch */
+#define FATTN_ERR_NOMEM (-4)       /* the split-K workspace could not be allocated */
+
+/* Element types of Q, K, V and O. LSE is always float32. */
+#define FATTN_F32 0
+#define FATTN_BF16 1
+
+/* Kernel families a configuration can name. */
+#define FATTN_KERNEL_AUTO 0
+#define FATTN_KERNEL_PREFILL_MFMA 1 /* bf16 matrix-core prefill */
+#define FATTN_KERNEL_PREFILL_F32 2  /* fp32 vector-ALU path (any Tq) */
+#define FATTN_KERNEL_DECODE_SPLITK 3 /* bf16 split-K decode + LSE combine (Tq == 1) */
+
+/* Launch configuration. A zero field means "use the tuned table's value". */
+typedef struct fattn_cfg {
+  int kernel;   /* FATTN_KERNEL_* */
+  int block_q;  /* query rows per workgroup (prefill: 32 * waves) */
+  int block_kv; /* keys per tile (prefill MFMA: 32 or 64; decode: 32) */
+  int waves;    /* wavefronts (64 lanes) per workgroup */
+  int splits;   /* decode: key-range splits per (batch, kv head) */
+  int schedule; /* prefill grid order: 1 = row-major, 2 = XCD-grouped, longest causal first */
+} fattn_cfg_t;
+
+/*
+ * attn_fwd: enqueue one forward pass on `stream` and return without waiting.
+ *
+ *   Q    [B, Hq,  Tq, d] contiguous, element type `dtype`
+ *   K, V [B, Hkv, Tk, d] contiguous, element type `dtype`
+ *   O    [B, Hq,  Tq, d] contiguous, element type `dtype` (written)
+ *   LSE  [B, Hq,  Tq]    contiguous float32, natural-log log-sum-exp of the scaled, masked
+ *                        scores of each row (written)
+ *
+ * All five pointers are device pointers on the current HIP device, owned by the caller, and must
+ * be 16-byte aligned. `scale` multiplies the dot products as given (callers usually pass
+ * 1/sqrt(d)); it must be finite. `causal` = 1 masks key j for query row i when
+ * j > i + (Tk - Tq): causal masks align at the bottom-right, so a single query row (Tq == 1)
+ * sees every key, the decode case. Hq must be a multiple of Hkv (grouped-query attention:
+ * query head h reads kv head h / (Hq / Hkv)). Tq == 1 with dtype bf16 runs the split-K decode
+ * kernels; any other shape runs the prefill kernels. `stream` is a hipStream_t (NULL = the
+ * default stream). O and LSE are valid once the stream reaches this point.
+ *
+ * Errors, all detected on the host before any HIP call:
+ *   FATTN_ERR_INVALID     a NULL pointer; B, Hq, Hkv, Tq, Tk or d negative; Tk == 0 with work
+ *                         to do; Hkv == 0 or Hq % Hkv != 0; causal not 0 or 1; causal with
+ *                         Tq > Tk (a row would see no key); a non-finite scale; an unknown
+ *                         dtype; a pointer not 16-byte aligned; Tq*d or Tk*d above 2^31 - 1.
+ *   FATTN_ERR_UNSUPPORTED d not in {32, 64, 128}.
+ * B == 0 or Tq == 0 (or Hq == 0) is a no-op that returns FATTN_OK.
+ * A launch failure returns FATTN_ERR_HIP; device faults surface at the caller's next
+ * synchronisation. The decode path allocates a grow-only workspace per device on first use
+ * (FATTN_ERR_NOMEM if that fails); fattn_release() frees it.
+ */
+int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+             int Hkv, int Tq, int Tk, int d, int causal, float scale, int dtype, void* stream);
+
+/*
+ * attn_fwd_cfg: attn_fwd with an explicit launch configuration (NULL = the tuned table).
+ * Non-zero fields override the table; a combination the kernels do not implement returns
+ * FATTN_ERR_UNSUPPORTED (for example block_kv not in {32, 64}, waves not in {4, 8}, or a decode
+ * kernel for a shape with Tq != 1). Used by the autotune sweep and the parity tests.
+ */
+int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+                 int Hkv, int Tq, int Tk, int d, int causal, float scale, int dtype, void* stream,
+                 const fattn_cfg_t* cfg);
+
+/*
+ * attn_fwd_plan: host-only query of the configuration attn_fwd would launch for this shape
+ * (after validation, with `cfg` overrides applied when non-NULL); writes it to *out.
+ * Same return codes as attn_fwd; makes no HIP call.
+ */
+int attn_fwd_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dtype,
+                  const fattn_cfg_t* cfg, fattn_cfg_t* out);
+
+/* Text for a return code (static storage). */
+const char* fattn_strerror(int code);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int fattn_version(void);
+
+/*
+ * Free the decode workspaces of every device after synchronising each device. Safe to call at
+ * any time when no call of this library is in flight; later calls allocate again.
+ */
+int fattn_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATTN_H */

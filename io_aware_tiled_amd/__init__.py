@@ -1,0 +1,173 @@
+"""Python binding of libfattn, the MI355X fused attention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+libfattn.so; torch supplies device memory and the current stream. Importing this package loads
+the in-tree library and fails loudly if it has not been built.
+
+    o, lse = attn_fwd(q, k, v, causal=True)      # q [B,Hq,Tq,d], k/v [B,Hkv,Tk,d] on the GPU
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fattn.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python io_aware_tiled_amd/build.py` "
+                      "(or __graft_entry__.build()) first")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+
+def _header_constants():
+    consts = {}
+    with open(HEADER_PATH) as f:
+        for m in re.finditer(r"#define\s+(FATTN_\w+)\s+\(?(-?\d+)\)?", f.read()):
+            consts[m.group(1)] = int(m.group(2))
+    return consts
+
+
+_C = _header_constants()
+FATTN_OK = _C["FATTN_OK"]
+FATTN_ERR_INVALID = _C["FATTN_ERR_INVALID"]
+FATTN_ERR_UNSUPPORTED = _C["FATTN_ERR_UNSUPPORTED"]
+FATTN_ERR_HIP = _C["FATTN_ERR_HIP"]
+FATTN_ERR_NOMEM = _C["FATTN_ERR_NOMEM"]
+FATTN_F32 = _C["FATTN_F32"]
+FATTN_BF16 = _C["FATTN_BF16"]
+FATTN_KERNEL_AUTO = _C["FATTN_KERNEL_AUTO"]
+FATTN_KERNEL_PREFILL_MFMA = _C["FATTN_KERNEL_PREFILL_MFMA"]
+FATTN_KERNEL_PREFILL_F32 = _C["FATTN_KERNEL_PREFILL_F32"]
+FATTN_KERNEL_DECODE_SPLITK = _C["FATTN_KERNEL_DECODE_SPLITK"]
+
+
+class FattnCfg(ctypes.Structure):
+    """Mirror of fattn_cfg_t."""
+
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("kernel", "block_q", "block_kv", "waves", "splits", "schedule")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_vp, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+_FWD_ARGS = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp]
+lib.attn_fwd.argtypes = _FWD_ARGS
+lib.attn_fwd.restype = _i
+lib.attn_fwd_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
+lib.attn_fwd_cfg.restype = _i
+lib.attn_fwd_plan.argtypes = [_i] * 8 + [ctypes.POINTER(FattnCfg), ctypes.POINTER(FattnCfg)]
+lib.attn_fwd_plan.restype = _i
+lib.fattn_strerror.argtypes = [_i]
+lib.fattn_strerror.restype = ctypes.c_char_p
+lib.fattn_version.argtypes = []
+lib.fattn_version.restype = _i
+lib.fattn_release.argtypes = []
+lib.fattn_release.restype = _i
+
+
+class FattnError(RuntimeError):
+    def __init__(self, code: int):
+        super().__init__(f"libfattn: {fattn_strerror(code)} (code {code})")
+        self.code = code
+
+
+def fattn_strerror(code: int) -> str:
+    return lib.fattn_strerror(int(code)).decode()
+
+
+def fattn_version() -> int:
+    return lib.fattn_version()
+
+
+def fattn_release() -> None:
+    rc = lib.fattn_release()
+    if rc != FATTN_OK:
+        raise FattnError(rc)
+
+
+def _make_cfg(cfg) -> Optional[FattnCfg]:
+    if cfg is None:
+        return None
+    if isinstance(cfg, FattnCfg):
+        return cfg
+    c = FattnCfg()
+    for k, v in dict(cfg).items():
+        setattr(c, k, int(v))
+    return c
+
+
+def attn_fwd_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg=None) -> dict:
+    """The launch configuration attn_fwd would use (host only, no GPU needed)."""
+    out = FattnCfg()
+    c = _make_cfg(cfg)
+    rc = lib.attn_fwd_plan(B, Hq, Hkv, Tq, Tk, d, int(causal), dtype,
+                           ctypes.byref(c) if c is not None else None, ctypes.byref(out))
+    if rc != FATTN_OK:
+        raise FattnError(rc)
+    return out.as_dict()
+
+
+def attn_fwd_raw(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream,
+                 cfg=None) -> int:
+    """The C call with plain integers for pointers; returns the library's status code."""
+    c = _make_cfg(cfg)
+    if c is None:
+        return lib.attn_fwd(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream)
+    return lib.attn_fwd_cfg(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream,
+                            ctypes.byref(c))
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None, lse=None,
+             cfg=None, stream=None) -> Tuple["object", "object"]:
+    """Fused attention forward on torch GPU tensors; returns (o, lse).
+
+    q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]; contiguous, all float32 or all bfloat16, on the
+    current device. o has q's dtype, lse is float32 [B, Hq, Tq] (natural log). scale defaults to
+    1/sqrt(d). The call is enqueued on `stream` (default: torch's current stream).
+    """
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dtype = FATTN_BF16
+    elif q.dtype == torch.float32:
+        dtype = FATTN_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, T, d]")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale), dtype, stream, cfg)
+    if rc != FATTN_OK:
+        raise FattnError(rc)
+    return out, lse

@@ -1,0 +1,269 @@
+// Host side of libfattn: argument validation, launch planning, the decode workspace and the
+// exported C entry points. Validation and planning make no HIP call, so every argument error is
+// reported identically on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "fattn.h"
+#include "kernels.h"
+#include "tune_table.h"
+
+namespace fattn {
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by attn_fwd_cfg and attn_fwd_plan. Sets *noop when there is no work.
+int validate_shape(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dtype,
+                   bool* noop) {
+  *noop = false;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Tq < 0 || Tk < 0 || d < 0) return FATTN_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FATTN_ERR_INVALID;
+  if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_ERR_INVALID;
+  if (B == 0 || Hq == 0 || Tq == 0) {
+    *noop = true;
+    return FATTN_OK;
+  }
+  if (Hkv == 0 || Hq % Hkv != 0) return FATTN_ERR_INVALID;
+  if (Tk == 0 || d == 0) return FATTN_ERR_INVALID;
+  if (causal && Tq > Tk) return FATTN_ERR_INVALID;
+  if (d != 32 && d != 64 && d != 128) return FATTN_ERR_UNSUPPORTED;
+  if ((long long)Tq * d > 0x7fffffffLL || (long long)Tk * d > 0x7fffffffLL)
+    return FATTN_ERR_INVALID;
+  return FATTN_OK;
+}
+
+// The configuration to launch: table defaults, then non-zero overrides from `cfg`.
+int make_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dtype,
+              const fattn_cfg_t* cfg, fattn_cfg_t* out) {
+  fattn_cfg_t p = {};
+  const bool decode_shape = (Tq == 1 && dtype == FATTN_BF16);
+  int kernel = (cfg && cfg->kernel) ? cfg->kernel : FATTN_KERNEL_AUTO;
+  if (kernel == FATTN_KERNEL_AUTO) {
+    kernel = dtype == FATTN_F32 ? FATTN_KERNEL_PREFILL_F32
+                                : (decode_shape ? FATTN_KERNEL_DECODE_SPLITK
+                                                : FATTN_KERNEL_PREFILL_MFMA);
+  }
+  p.kernel = kernel;
+  switch (kernel) {
+    case FATTN_KERNEL_PREFILL_F32:
+      if (dtype != FATTN_F32) return FATTN_ERR_UNSUPPORTED;
+      p.block_q = 64;
+      p.block_kv = 32;
+      p.waves = 1;
+      p.splits = 1;
+      p.schedule = 1;
+      if (cfg && ((cfg->block_q && cfg->block_q != 64) || (cfg->block_kv && cfg->block_kv != 32) ||
+                  (cfg->waves && cfg->waves != 1) || (cfg->splits && cfg->splits != 1)))
+        return FATTN_ERR_UNSUPPORTED;
+      break;
+    case FATTN_KERNEL_PREFILL_MFMA: {
+      if (dtype != FATTN_BF16) return FATTN_ERR_UNSUPPORTED;
+      const PrefillEntry* e = nullptr;
+      for (const PrefillEntry& r : kPrefillTable) {
+        if (r.d == d && (r.causal < 0 || r.causal == causal) && (r.tk_max == 0 || Tk <= r.tk_max)) {
+          e = &r;
+          break;
+        }
+      }
+      if (!e) return FATTN_ERR_UNSUPPORTED;
+      p.block_kv = e->block_kv;
+      p.waves = e->waves;
+      p.schedule = e->schedule;
+      p.splits = 1;
+      if (cfg) {
+        if (cfg->block_kv) p.block_kv = cfg->block_kv;
+        if (cfg->waves) p.waves = cfg->waves;
+        if (cfg->schedule) p.schedule = cfg->schedule;
+        if (cfg->splits && cfg->splits != 1) return FATTN_ERR_UNSUPPORTED;
+      }
+      if (p.block_kv != 32 && p.block_kv != 64) return FATTN_ERR_UNSUPPORTED;
+      if (p.waves != 4 && p.waves != 8) return FATTN_ERR_UNSUPPORTED;
+      if (p.schedule != 1 && p.schedule != 2) return FATTN_ERR_UNSUPPORTED;
+      p.block_q = 32 * p.waves;
+      if (cfg && cfg->block_q && cfg->block_q != p.block_q) return FATTN_ERR_UNSUPPORTED;
+      break;
+    }
+    case FATTN_KERNEL_DECODE_SPLITK: {
+      if (dtype != FATTN_BF16 || Tq != 1) return FATTN_ERR_UNSUPPORTED;
+      const DecodeEntry* e = nullptr;
+      for (const DecodeEntry& r : kDecodeTable)
+        if (r.d == d) e = &r;
+      if (!e) return FATTN_ERR_UNSUPPORTED;
+      const int G = Hq / Hkv;
+      const long long units = (long long)B * Hkv * ((G + 15) / 16);
+      const int max_splits = (Tk + 31) / 32;
+      int splits;
+      if (cfg && cfg->splits) {
+        splits = cfg->splits;
+        if (splits < 1) return FATTN_ERR_UNSUPPORTED;
+      } else {
+        long long want = (e->target_workgroups + units - 1) / units;
+        const int by_chunk = (Tk + e->min_chunk - 1) / e->min_chunk;
+        if (want > by_chunk) want = by_chunk;
+        if (want < 1) want = 1;
+        splits = (int)want;
+      }
+      if (splits > max_splits) splits = max_splits;
+      // keys per split, rounded up to the 32-key block; drop splits that would be empty
+      int chunk = ((Tk + splits - 1) / splits + 31) / 32 * 32;
+      splits = (Tk + chunk - 1) / chunk;
+      p.splits = splits;
+      p.block_kv = 32;
+      p.block_q = 16;
+      p.waves = 1;
+      p.schedule = 1;
+      if (cfg && ((cfg->block_kv && cfg->block_kv != 32) || (cfg->waves && cfg->waves != 1)))
+        return FATTN_ERR_UNSUPPORTED;
+      break;
+    }
+    default:
+      return FATTN_ERR_UNSUPPORTED;
+  }
+  *out = p;
+  return FATTN_OK;
+}
+
+// Grow-only decode workspace per (device, stream). The lock is held across the launches that
+// use it, so a buffer is never replaced while a call is between lookup and enqueue.
+struct Workspace {
+  float* ptr = nullptr;
+  size_t floats = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+}  // namespace
+}  // namespace fattn
+
+using namespace fattn;
+
+extern "C" int attn_fwd_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dtype,
+                             const fattn_cfg_t* cfg, fattn_cfg_t* out) {
+  if (!out) return FATTN_ERR_INVALID;
+  bool noop;
+  int rc = validate_shape(B, Hq, Hkv, Tq, Tk, d, causal, dtype, &noop);
+  if (rc != FATTN_OK) return rc;
+  if (noop) {
+    *out = fattn_cfg_t{};
+    return FATTN_OK;
+  }
+  return make_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg, out);
+}
+
+extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+                            int dtype, void* stream, const fattn_cfg_t* cfg) {
+  bool noop;
+  int rc = validate_shape(B, Hq, Hkv, Tq, Tk, d, causal, dtype, &noop);
+  if (rc != FATTN_OK) return rc;
+  if (!std::isfinite(scale)) return FATTN_ERR_INVALID;
+  if (noop) return FATTN_OK;
+  if (!Q || !K || !V || !O || !LSE) return FATTN_ERR_INVALID;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return FATTN_ERR_INVALID;
+  fattn_cfg_t plan;
+  rc = make_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg, &plan);
+  if (rc != FATTN_OK) return rc;
+
+  Problem p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.LSE = LSE;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Tq = Tq;
+  p.Tk = Tk;
+  p.d = d;
+  p.causal = causal;
+  p.qsign = scale > 0.f ? 1 : (scale < 0.f ? -1 : 0);
+  p.abs_scale = scale == 0.f ? 1.f : std::fabs(scale);
+  p.log2_scale = p.abs_scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  hipError_t e = hipSuccess;
+  switch (plan.kernel) {
+    case FATTN_KERNEL_PREFILL_F32:
+      e = launch_prefill_f32(p, s);
+      break;
+    case FATTN_KERNEL_PREFILL_MFMA:
+      e = launch_prefill_bf16(p, plan.block_kv, plan.waves, plan.schedule, s);
+      break;
+    case FATTN_KERNEL_DECODE_SPLITK: {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess) return FATTN_ERR_HIP;
+      const int chunk = ((Tk + plan.splits - 1) / plan.splits + 31) / 32 * 32;
+      const size_t rows = (size_t)B * Hq * plan.splits;
+      const size_t need = rows * (size_t)d + rows;
+      std::lock_guard<std::mutex> lock(g_ws_mutex);
+      Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
+      if (ws.floats < need) {
+        if (ws.ptr) {
+          if (hipStreamSynchronize(s) != hipSuccess) return FATTN_ERR_HIP;
+          (void)hipFree(ws.ptr);
+          ws.ptr = nullptr;
+          ws.floats = 0;
+        }
+        void* mem = nullptr;
+        if (hipMalloc(&mem, need * sizeof(float)) != hipSuccess) {
+          (void)hipGetLastError();
+          return FATTN_ERR_NOMEM;
+        }
+        ws.ptr = static_cast<float*>(mem);
+        ws.floats = need;
+      }
+      e = launch_decode_bf16(p, plan.splits, chunk, ws.ptr, ws.ptr + rows * (size_t)d, s);
+      break;
+    }
+    default:
+      return FATTN_ERR_UNSUPPORTED;
+  }
+  return e == hipSuccess ? FATTN_OK : FATTN_ERR_HIP;
+}
+
+extern "C" int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                        int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale, int dtype,
+                        void* stream) {
+  return attn_fwd_cfg(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream,
+                      nullptr);
+}
+
+extern "C" const char* fattn_strerror(int code) {
+  switch (code) {
+    case FATTN_OK: return "ok";
+    case FATTN_ERR_INVALID: return "invalid argument";
+    case FATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FATTN_ERR_HIP: return "HIP runtime error";
+    case FATTN_ERR_NOMEM: return "out of device memory for the decode workspace";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int fattn_version(void) { return kVersion; }
+
+extern "C" int fattn_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int rc = FATTN_OK;
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_ws) {
+    if (!kv.second.ptr) continue;
+    if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+        hipFree(kv.second.ptr) != hipSuccess)
+      rc = FATTN_ERR_HIP;
+  }
+  g_ws.clear();
+  if (have_cur) (void)hipSetDevice(cur);
+  return rc;
+}

@@ -1,0 +1,253 @@
+// bf16 decode (one query token per head) for gfx950: split-K partial kernel + LSE combine.
+//
+// A decode step reads every cached key and value once and does about eight FLOPs per byte under
+// 8-way grouped-query attention, so it is bound by HBM bandwidth ("Attention from scratch +
+// roofline", section "Classify prefill vs decode", and its exercise 1 on GQA). The key range of
+// each (batch, kv head) is therefore split into `splits` chunks processed by independent
+// single-wavefront workgroups, so that thousands of wavefronts keep loads in flight. Each chunk
+// runs the online-softmax recurrence of "4.2 FlashAttention I" over its keys and writes a
+// normalised partial output O_s with its log-sum-exp LSE_s; the combine kernel then merges the
+// chunks exactly, O = sum_s exp(LSE_s - LSE) O_s with LSE = log sum_s exp(LSE_s), which holds
+// because any reference maximum gives the same final ratio ("Efficient attention & KV cache",
+// section 2.1).
+//
+// Inside a chunk the G query heads that share a kv head form the 16-wide N side of
+// v_mfma_f32_16x16x32_bf16 (padded with zero rows when G < 16): S^T = K Q^T takes K straight
+// from global memory in the operand layout, and O^T = V^T P^T reads V^T from a small per-wave
+// LDS transpose whose key order matches the S^T accumulator, as in the prefill kernel.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace fattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kNegInf = -__builtin_inff();
+constexpr int KB = 32;       // keys per block
+constexpr int VS = KB + 8;   // LDS row pitch of V^T (elements): +16 bytes
+
+__device__ __forceinline__ uint32_t pick_half(uint32_t a, uint32_t b, int hi) {
+  return hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+}
+
+template <int D>
+struct Block {
+  u32x4 k[2][D / 32];  // K rows kb+16t+lane%16, dims 32c + 8*(lane/16) .. +8
+  u32x4 v[8];          // V rows of keys 4gg+r and 16+4gg+r, dims 8dg .. 8dg+8
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(Block<D>& blk, const __bf16* Kh, const __bf16* Vh,
+                                           int kb, int kend, int lane) {
+  const int c16 = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int key = kb + 16 * t + c16;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < kend) x = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + 32 * c + 8 * g4);
+      blk.k[t][c] = x;
+    }
+  }
+  if (lane < D / 2) {
+    const int gg = lane & 3, dg = lane >> 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = kb + 4 * gg + (i & 3) + 16 * (i >> 2);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < kend) x = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + 8 * dg);
+      blk.v[i] = x;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64, 2) void decode_partial_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hq, int Hkv, int Tk, int splits,
+    int chunk, float log2_scale, int qsign) {
+  __shared__ __align__(16) __bf16 Vt[D * VS];
+
+  const int lane = threadIdx.x;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int G = Hq / Hkv;
+  const int nqg = (G + 15) / 16;
+  int w = blockIdx.x;
+  const int s = w % splits;
+  w /= splits;
+  const int qg = w % nqg;
+  w /= nqg;
+  const int hk = w % Hkv;
+  const int b = w / Hkv;
+  const int kbeg = s * chunk;
+  const int kend = min(Tk, kbeg + chunk);
+  const int qi = qg * 16 + c16;
+  const bool qvalid = qi < G;
+  const int hq = hk * G + qi;
+
+  // Q^T operand: column = query qi, dims 32c + 8*g4 .. +8
+  bf16x8 qb[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (qvalid && qsign != 0) {
+      raw = *reinterpret_cast<const u32x4*>(Q + ((size_t)b * Hq + hq) * D + 32 * c + 8 * g4);
+      if (qsign < 0) raw ^= 0x80008000u;
+    }
+    qb[c] = __builtin_bit_cast(bf16x8, raw);
+  }
+
+  const __bf16* Kh = K + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
+  const __bf16* Vh = V + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
+
+  float M = kNegInf, lsum = 0.f;
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) acc[mt] = f32x4{};
+
+  Block<D> cur;
+  if (kbeg < kend) load_block<D>(cur, Kh, Vh, kbeg, kend, lane);
+
+  for (int kb = kbeg; kb < kend; kb += KB) {
+    const bool more = kb + KB < kend;
+    Block<D> nxt;
+    if (more) load_block<D>(nxt, Kh, Vh, kb + KB, kend, lane);
+
+    __syncthreads();  // the previous block's V^T reads are done
+    if (lane < D / 2) {
+      const int gg = lane & 3, dg = lane >> 2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wd = e >> 1, hi = e & 1;
+        u32x4 row = {pick_half(cur.v[0][wd], cur.v[1][wd], hi),
+                     pick_half(cur.v[2][wd], cur.v[3][wd], hi),
+                     pick_half(cur.v[4][wd], cur.v[5][wd], hi),
+                     pick_half(cur.v[6][wd], cur.v[7][wd], hi)};
+        *reinterpret_cast<u32x4*>(Vt + (8 * dg + e) * VS + 8 * gg) = row;
+      }
+    }
+
+    // S^T: rows = keys kb + 16t + 4*g4 + r, column = query qi
+    f32x4 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = f32x4{};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[t][c]),
+                                                       qb[c], st[t], 0, 0, 0);
+    }
+    if (kb + KB > kend) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kb + 16 * t + 4 * g4 + r >= kend) st[t][r] = kNegInf;
+    }
+
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(M, mx * log2_scale);
+    const float base = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(M - base);
+    M = m_new;
+    bf16x8 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(st[i >> 2][i & 3], log2_scale, -base));
+      psum += p;
+      pb[i] = (__bf16)p;
+    }
+    lsum = fmaf(alpha, lsum, psum);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) acc[mt] *= alpha;
+
+    __syncthreads();  // V^T of this block is in LDS
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + (16 * mt + c16) * VS + 8 * g4);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[mt], 0, 0, 0);
+    }
+    if (more) cur = nxt;
+  }
+
+  float l = lsum + __shfl_xor(lsum, 16);
+  l += __shfl_xor(l, 32);
+  if (!qvalid) return;
+  const size_t slot = ((size_t)b * Hq + hq) * splits + s;
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt)
+    *reinterpret_cast<f32x4*>(ws_o + slot * D + 16 * mt + 4 * g4) = acc[mt] * inv;
+  if (g4 == 0) ws_lse[slot] = (l > 0.f) ? (M + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void decode_combine_kernel(const float* __restrict__ ws_o,
+                                                             const float* __restrict__ ws_lse,
+                                                             __bf16* __restrict__ O,
+                                                             float* __restrict__ LSE,
+                                                             int splits) {
+  const size_t row = blockIdx.x;  // b * Hq + h
+  const int d = threadIdx.x;
+  const float* lp = ws_lse + row * splits;
+  float mx = kNegInf;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, lp[s]);
+  const float base = (mx == kNegInf) ? 0.f : mx;
+  float tot = 0.f, o = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float w = expf(lp[s] - base);
+    tot += w;
+    o = fmaf(w, ws_o[(row * splits + s) * D + d], o);
+  }
+  O[row * D + d] = (__bf16)(o / tot);
+  if (d == 0) LSE[row] = base + logf(tot);
+}
+
+template <int D>
+hipError_t launch_t(const Problem& p, int splits, int chunk, float* ws_o, float* ws_lse,
+                    hipStream_t stream) {
+  const int G = p.Hq / p.Hkv;
+  const int nqg = (G + 15) / 16;
+  const long long grid = (long long)p.B * p.Hkv * nqg * splits;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL || (long long)p.B * p.Hq > 0x7fffffffLL)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(decode_partial_kernel<D>, dim3((unsigned)grid), dim3(64), 0, stream,
+                     static_cast<const __bf16*>(p.Q), static_cast<const __bf16*>(p.K),
+                     static_cast<const __bf16*>(p.V), ws_o, ws_lse, p.Hq, p.Hkv, p.Tk, splits,
+                     chunk, p.log2_scale, p.qsign);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(D), 0, stream,
+                     ws_o, ws_lse, static_cast<__bf16*>(p.O), p.LSE, splits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const Problem& p, int splits, int chunk, float* ws_o,
+                              float* ws_lse, hipStream_t stream) {
+  switch (p.d) {
+    case 32: return launch_t<32>(p, splits, chunk, ws_o, ws_lse, stream);
+    case 64: return launch_t<64>(p, splits, chunk, ws_o, ws_lse, stream);
+    case 128: return launch_t<128>(p, splits, chunk, ws_o, ws_lse, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fattn

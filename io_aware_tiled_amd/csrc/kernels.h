@@ -1,0 +1,40 @@
+// Internal launch interface between the host library (api.cpp) and the HIP kernels.
+// Every launcher enqueues on `stream`, returns the launch status and performs no allocation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fattn {
+
+// Host-side view of one forward problem. Pointers are device pointers; element type is implied
+// by the launcher. `log2_scale` is |scale| * log2(e) (1 when scale == 0) and `qsign` is the
+// sign of scale (-1, 0 or +1): the kernels multiply Q by qsign as they load it, which is exact,
+// so every kernel works with a positive scale.
+struct Problem {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* LSE;
+  int B, Hq, Hkv, Tq, Tk, d;
+  int causal;
+  float abs_scale;   // |scale|, or 1 when scale == 0
+  float log2_scale;  // abs_scale * log2(e)
+  int qsign;
+};
+
+// bf16 matrix-core prefill. block_kv in {32, 64}, waves in {4, 8}, d in {32, 64, 128};
+// schedule 1 = row-major grid, 2 = XCD-grouped with the longest causal blocks first.
+hipError_t launch_prefill_bf16(const Problem& p, int block_kv, int waves, int schedule,
+                               hipStream_t stream);
+
+// fp32 vector-ALU path, any Tq (also Tq == 1), d in {32, 64, 128}.
+hipError_t launch_prefill_f32(const Problem& p, hipStream_t stream);
+
+// bf16 split-K decode (Tq == 1): partial kernel + combine kernel on the same stream.
+// ws_o holds splits * B * Hq * d floats, ws_lse splits * B * Hq floats.
+// chunk is the number of keys per split (a multiple of 32); splits = ceil(Tk / chunk).
+hipError_t launch_decode_bf16(const Problem& p, int splits, int chunk, float* ws_o,
+                              float* ws_lse, hipStream_t stream);
+
+}  // namespace fattn

@@ -1,0 +1,45 @@
+// Launch-configuration table of libfattn.
+//
+// The block size is a performance choice, not a numerical one ("SDPA and FlashAttention's
+// tiling", section "A softmax you can compute one block at a time"; "Explain tiled attention and
+// verify its output", section "Separate storage savings from runtime": tile size, register
+// pressure and cache reuse decide the speed). Every entry computes the same function; the
+// parity tests run each one.
+//
+// Prefill rows are matched in order: the first row whose d matches, whose causal flag matches
+// (-1 = either) and whose Tk is at most tk_max (0 = no bound) wins.
+#pragma once
+
+namespace fattn {
+
+struct PrefillEntry {
+  int d;
+  int causal;   // -1 = any
+  int tk_max;   // 0 = unbounded
+  int block_kv;
+  int waves;
+  int schedule;
+};
+
+static const PrefillEntry kPrefillTable[] = {
+    // d, causal, tk_max, block_kv, waves, schedule
+    {64, -1, 0, 64, 4, 2},
+    {128, -1, 0, 64, 4, 2},
+    {32, -1, 0, 64, 4, 2},
+};
+
+// Decode: number of workgroups to aim for across the whole grid and the smallest key chunk a
+// split may have (keys, multiple of 32).
+struct DecodeEntry {
+  int d;
+  int target_workgroups;
+  int min_chunk;
+};
+
+static const DecodeEntry kDecodeTable[] = {
+    {128, 2048, 256},
+    {64, 2048, 256},
+    {32, 2048, 256},
+};
+
+}  // namespace fattn
