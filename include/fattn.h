@@ -104,6 +104,13 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int
 /* Text for a return code (static storage). */
 const char* fattn_strerror(int code);
 
+/*
+ * Text describing the most recent failure of a call on the calling thread: which check failed or
+ * which HIP call returned which error. Empty after a successful call. Thread-local storage, valid
+ * until the thread's next call into the library.
+ */
+const char* fattn_last_error(void);
+
 /* Library version as major * 10000 + minor * 100 + patch. */
 int fattn_version(void);
 

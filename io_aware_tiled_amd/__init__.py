@@ -23,6 +23,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python io_aware_tiled_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
+# torch is imported first so that its bundled HIP runtime is the one in the process: libfattn
+# needs libamdhip64.so.7 by soname and then binds to that same runtime, which is the one that
+# owns the streams and device pointers torch hands over. (Loaded the other way round, the
+# system runtime and torch's bundled HSA runtime would be mixed in one process.)
+import torch  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 
 
@@ -68,6 +74,8 @@ lib.attn_fwd_plan.argtypes = [_i] * 8 + [ctypes.POINTER(FattnCfg), ctypes.POINTE
 lib.attn_fwd_plan.restype = _i
 lib.fattn_strerror.argtypes = [_i]
 lib.fattn_strerror.restype = ctypes.c_char_p
+lib.fattn_last_error.argtypes = []
+lib.fattn_last_error.restype = ctypes.c_char_p
 lib.fattn_version.argtypes = []
 lib.fattn_version.restype = _i
 lib.fattn_release.argtypes = []
@@ -75,9 +83,16 @@ lib.fattn_release.restype = _i
 
 
 class FattnError(RuntimeError):
-    def __init__(self, code: int):
-        super().__init__(f"libfattn: {fattn_strerror(code)} (code {code})")
+    def __init__(self, code: int, detail: str = ""):
+        msg = f"libfattn: {fattn_strerror(code)} (code {code})"
+        super().__init__(msg + (f": {detail}" if detail else ""))
         self.code = code
+        self.detail = detail
+
+
+def fattn_last_error() -> str:
+    """Why the calling thread's most recent library call failed ('' after a success)."""
+    return lib.fattn_last_error().decode()
 
 
 def fattn_strerror(code: int) -> str:
@@ -112,7 +127,7 @@ def attn_fwd_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg=None) -> dict:
     rc = lib.attn_fwd_plan(B, Hq, Hkv, Tq, Tk, d, int(causal), dtype,
                            ctypes.byref(c) if c is not None else None, ctypes.byref(out))
     if rc != FATTN_OK:
-        raise FattnError(rc)
+        raise FattnError(rc, fattn_last_error())
     return out.as_dict()
 
 
@@ -169,5 +184,5 @@ def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=N
     rc = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale), dtype, stream, cfg)
     if rc != FATTN_OK:
-        raise FattnError(rc)
+        raise FattnError(rc, fattn_last_error())
     return out, lse

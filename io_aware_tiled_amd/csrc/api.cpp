@@ -4,7 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdarg>
 #include <cstdint>
+#include <cstdio>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -21,23 +23,40 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+thread_local char g_last_error[256] = "";
+
+// Records why a call failed (per thread) and returns `code`.
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(int code, const char* what, hipError_t e) {
+  return fail(code, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
 // Shape checks shared by attn_fwd_cfg and attn_fwd_plan. Sets *noop when there is no work.
 int validate_shape(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dtype,
                    bool* noop) {
   *noop = false;
-  if (B < 0 || Hq < 0 || Hkv < 0 || Tq < 0 || Tk < 0 || d < 0) return FATTN_ERR_INVALID;
-  if (causal != 0 && causal != 1) return FATTN_ERR_INVALID;
-  if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_ERR_INVALID;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Tq < 0 || Tk < 0 || d < 0)
+    return fail(FATTN_ERR_INVALID, "negative dimension");
+  if (causal != 0 && causal != 1) return fail(FATTN_ERR_INVALID, "causal must be 0 or 1");
+  if (dtype != FATTN_F32 && dtype != FATTN_BF16) return fail(FATTN_ERR_INVALID, "unknown dtype");
   if (B == 0 || Hq == 0 || Tq == 0) {
     *noop = true;
     return FATTN_OK;
   }
-  if (Hkv == 0 || Hq % Hkv != 0) return FATTN_ERR_INVALID;
-  if (Tk == 0 || d == 0) return FATTN_ERR_INVALID;
-  if (causal && Tq > Tk) return FATTN_ERR_INVALID;
-  if (d != 32 && d != 64 && d != 128) return FATTN_ERR_UNSUPPORTED;
+  if (Hkv == 0 || Hq % Hkv != 0) return fail(FATTN_ERR_INVALID, "Hq must be a multiple of Hkv");
+  if (Tk == 0) return fail(FATTN_ERR_INVALID, "Tk == 0: softmax over no keys");
+  if (d == 0) return fail(FATTN_ERR_INVALID, "d == 0");
+  if (causal && Tq > Tk) return fail(FATTN_ERR_INVALID, "causal with Tq > Tk");
+  if (d != 32 && d != 64 && d != 128) return fail(FATTN_ERR_UNSUPPORTED, "head dim %d", d);
   if ((long long)Tq * d > 0x7fffffffLL || (long long)Tk * d > 0x7fffffffLL)
-    return FATTN_ERR_INVALID;
+    return fail(FATTN_ERR_INVALID, "T*d exceeds 2^31-1");
   return FATTN_OK;
 }
 
@@ -148,7 +167,8 @@ using namespace fattn;
 
 extern "C" int attn_fwd_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dtype,
                              const fattn_cfg_t* cfg, fattn_cfg_t* out) {
-  if (!out) return FATTN_ERR_INVALID;
+  g_last_error[0] = 0;
+  if (!out) return fail(FATTN_ERR_INVALID, "out is NULL");
   bool noop;
   int rc = validate_shape(B, Hq, Hkv, Tq, Tk, d, causal, dtype, &noop);
   if (rc != FATTN_OK) return rc;
@@ -156,23 +176,25 @@ extern "C" int attn_fwd_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int 
     *out = fattn_cfg_t{};
     return FATTN_OK;
   }
-  return make_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg, out);
+  rc = make_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg, out);
+  return rc == FATTN_OK ? rc : fail(rc, "launch configuration not implemented for this shape");
 }
 
 extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O, float* LSE,
                             int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
                             int dtype, void* stream, const fattn_cfg_t* cfg) {
+  g_last_error[0] = 0;
   bool noop;
   int rc = validate_shape(B, Hq, Hkv, Tq, Tk, d, causal, dtype, &noop);
   if (rc != FATTN_OK) return rc;
-  if (!std::isfinite(scale)) return FATTN_ERR_INVALID;
+  if (!std::isfinite(scale)) return fail(FATTN_ERR_INVALID, "scale is not finite");
   if (noop) return FATTN_OK;
-  if (!Q || !K || !V || !O || !LSE) return FATTN_ERR_INVALID;
+  if (!Q || !K || !V || !O || !LSE) return fail(FATTN_ERR_INVALID, "NULL tensor pointer");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
-    return FATTN_ERR_INVALID;
+    return fail(FATTN_ERR_INVALID, "tensor pointer not 16-byte aligned");
   fattn_cfg_t plan;
   rc = make_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg, &plan);
-  if (rc != FATTN_OK) return rc;
+  if (rc != FATTN_OK) return fail(rc, "launch configuration not implemented for this shape");
 
   Problem p;
   p.Q = Q;
@@ -202,7 +224,8 @@ extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O
       break;
     case FATTN_KERNEL_DECODE_SPLITK: {
       int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess) return FATTN_ERR_HIP;
+      hipError_t he = hipGetDevice(&dev);
+      if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipGetDevice", he);
       const int chunk = ((Tk + plan.splits - 1) / plan.splits + 31) / 32 * 32;
       const size_t rows = (size_t)B * Hq * plan.splits;
       const size_t need = rows * (size_t)d + rows;
@@ -210,15 +233,17 @@ extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O
       Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
       if (ws.floats < need) {
         if (ws.ptr) {
-          if (hipStreamSynchronize(s) != hipSuccess) return FATTN_ERR_HIP;
+          he = hipStreamSynchronize(s);
+          if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipStreamSynchronize", he);
           (void)hipFree(ws.ptr);
           ws.ptr = nullptr;
           ws.floats = 0;
         }
         void* mem = nullptr;
-        if (hipMalloc(&mem, need * sizeof(float)) != hipSuccess) {
+        he = hipMalloc(&mem, need * sizeof(float));
+        if (he != hipSuccess) {
           (void)hipGetLastError();
-          return FATTN_ERR_NOMEM;
+          return hip_fail(FATTN_ERR_NOMEM, "hipMalloc of the decode workspace", he);
         }
         ws.ptr = static_cast<float*>(mem);
         ws.floats = need;
@@ -227,9 +252,9 @@ extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O
       break;
     }
     default:
-      return FATTN_ERR_UNSUPPORTED;
+      return fail(FATTN_ERR_UNSUPPORTED, "unknown kernel family");
   }
-  return e == hipSuccess ? FATTN_OK : FATTN_ERR_HIP;
+  return e == hipSuccess ? FATTN_OK : hip_fail(FATTN_ERR_HIP, "kernel launch", e);
 }
 
 extern "C" int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
@@ -249,6 +274,8 @@ extern "C" const char* fattn_strerror(int code) {
     default: return "unknown error code";
   }
 }
+
+extern "C" const char* fattn_last_error(void) { return g_last_error; }
 
 extern "C" int fattn_version(void) { return kVersion; }
 

@@ -124,6 +124,13 @@ def test_python_binding_raises_with_code():
     with pytest.raises(fa.FattnError) as e:
         fa.attn_fwd_plan(1, 8, 3, 64, 64, 64, True, BF16)
     assert e.value.code == INVALID
+    assert "multiple of Hkv" in e.value.detail
+
+
+def test_last_error_text_follows_each_call():
+    assert _call(d=96) == UNSUPPORTED and "96" in fa.fattn_last_error()
+    assert _call(Q=P + 2) == INVALID and "aligned" in fa.fattn_last_error()
+    assert _call(B=0) == OK and fa.fattn_last_error() == ""
 
 
 def test_python_binding_rejects_cpu_tensors():

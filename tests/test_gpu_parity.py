@@ -54,12 +54,12 @@ def run_gpu(fa, Q, K, V, causal, scale, dtype, cfg=None):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def check(o, l, o_ref, l_ref, dtype, what=""):
+def check(o, l, o_ref, l_ref, dtype, what="", f32_bound=F32_MAX_ABS):
     eo, el = np.abs(o - o_ref), np.abs(l - l_ref)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(l)), what
     if dtype == "f32":
-        assert eo.max() <= F32_MAX_ABS, (what, "O", eo.max())
-        assert el.max() <= F32_MAX_ABS, (what, "LSE", el.max())
+        assert eo.max() <= f32_bound, (what, "O", eo.max())
+        assert el.max() <= f32_bound, (what, "LSE", el.max())
     else:
         assert eo.max() <= BF16_MAX_ABS, (what, "O", eo.max())
         assert el.max() <= BF16_MAX_ABS, (what, "LSE", el.max())
@@ -67,12 +67,19 @@ def check(o, l, o_ref, l_ref, dtype, what=""):
         assert el.sum() <= BF16_MEAN_REL * max(np.abs(l_ref).sum(), 1e-30), (what, "LSE mean-rel")
 
 
+def f32_bound_for_scale(scale, d):
+    """fp32 bound for a literal scale: 1e-5 up to the default 1/sqrt(d), growing in proportion
+    beyond it, because a logit's fp32 rounding error is proportional to its magnitude (about
+    |scale| * sqrt(d) for unit-variance q and k) and the output error follows it."""
+    return F32_MAX_ABS * max(1.0, abs(scale) * math.sqrt(d))
+
+
 def full_case(fa, cfg: AttnConfig, launch=None, scale=None):
     Q, K, V = inputs.make_inputs(cfg)
     sc = cfg.scale if scale is None else scale
     o, l = run_gpu(fa, Q, K, V, cfg.causal, sc, cfg.dtype, launch)
     o_ref, l_ref = oracle.dense_attention(Q, K, V, cfg.causal, sc)
-    check(o, l, o_ref, l_ref, cfg.dtype, f"{cfg.name} {launch}")
+    check(o, l, o_ref, l_ref, cfg.dtype, f"{cfg.name} {launch}", f32_bound_for_scale(sc, cfg.d))
     return o, l
 
 
