@@ -1,0 +1,242 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--cpu-baseline auto|off]
+
+One step is one pass of the whole hot path on synthetic, seeded inputs already resident in HBM:
+  * causal prefill, bf16, B=1, H=32, T=8192, d=128 (one attn_fwd call: the MFMA prefill kernel);
+  * GQA decode, bf16, B=64, Hq=64, Hkv=8, Tq=1, Tk=8192, d=128 (one attn_fwd call: split-K
+    partial kernel + combine kernel).
+Each call is bracketed by HIP events recorded on the stream the kernels are launched on. The
+headline value is the prefill rate in TFLOP/s, counting 4*B*H*T^2*d halved for the causal mask;
+the decode rate is reported as algorithmic HBM bytes per second (K and V read once, Q read,
+O and LSE written). One JSON line is printed.
+
+    python bench.py --calibrate-copy BYTES
+
+runs a device-to-device copy of BYTES bytes a few times (for scaling hardware byte counters) and
+prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal prefill TFLOP/s (% MFMA peak) at T=8192,d=128; decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+PREFILL = "c3_bf16_causal_t8192_d128"
+DECODE = "c4_bf16_gqa_decode_tk8192_d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def prefill_flops(B, H, Tq, Tk, d, causal):
+    """4*B*H*Tq*Tk*d, halved under a causal mask."""
+    f = 4.0 * B * H * Tq * Tk * d
+    return f / 2 if causal else f
+
+
+def decode_bytes(B, Hq, Hkv, Tk, d, eb=2):
+    """K and V read once, Q read, O written (element size eb), LSE written in fp32."""
+    return (2 * B * Hkv * Tk * d + 2 * B * Hq * d) * eb + 4 * B * Hq
+
+
+def source_hash(name):
+    with open(os.path.join(ROOT, "io_aware_tiled_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def device_inputs(cfg, torch):
+    """Seeded inputs, generated head by head on the host and copied to the GPU."""
+    from tests import inputs
+
+    def build(which, H, T):
+        t = torch.empty((cfg.B, H, T, cfg.d), dtype=torch.bfloat16, device="cuda")
+        for b in range(cfg.B):
+            for h in range(H):
+                t[b, h].copy_(inputs.to_torch(inputs.head_slice(cfg, which, b, h), "bf16"))
+        return t
+
+    return (build(inputs.Q_ID, cfg.Hq, cfg.Tq), build(inputs.K_ID, cfg.Hkv, cfg.Tk),
+            build(inputs.V_ID, cfg.Hkv, cfg.Tk))
+
+
+def traffic_for(kernel_source, launches_key):
+    """HBM bytes per launch from the committed counter summary, or None if it is missing or the
+    kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(launches_key)
+    if not ent or ent.get("source_sha256_16") != source_hash(kernel_source):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s=12.0, max_heads=32):
+    """The fp64 oracle timed on the host cores on a bounded sample of the prefill workload."""
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from tests import inputs
+
+    cfg = inputs.CONFIGS[PREFILL]
+    heads, elapsed = 0, 0.0
+    while heads < max_heads and (heads == 0 or elapsed < budget_s):
+        q = inputs.head_slice(cfg, inputs.Q_ID, 0, heads)
+        k = inputs.head_slice(cfg, inputs.K_ID, 0, heads)
+        v = inputs.head_slice(cfg, inputs.V_ID, 0, heads)
+        t0 = time.perf_counter()
+        oracle.dense_head(q, k, v, cfg.causal, cfg.scale)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+    flops = prefill_flops(1, heads, cfg.Tq, cfg.Tk, cfg.d, cfg.causal)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of 32 heads of the causal T=8192 d=128 prefill, all 8192 rows "
+                      f"each, fp64 dense (S and P materialised), {elapsed:.2f} s; TFLOP/s with "
+                      f"the same causal-halved FLOP count as the GPU figure",
+            "seconds": elapsed, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def calibrate_copy(nbytes, reps=3):
+    import torch
+
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-baseline", choices=["auto", "off"], default="auto")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this build has no multi-GPU path; shard (batch, kv-head) groups across GPUs "
+              "with one process each instead.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    import io_aware_tiled_amd as fa
+    from tests import inputs
+
+    pc, dc = inputs.CONFIGS[PREFILL], inputs.CONFIGS[DECODE]
+    print(f"[bench] generating inputs: {pc.name}, {dc.name}", file=sys.stderr, flush=True)
+    q3, k3, v3 = device_inputs(pc, torch)
+    q4, k4, v4 = device_inputs(dc, torch)
+    o3, l3 = torch.empty_like(q3), torch.empty(pc.B, pc.Hq, pc.Tq, device="cuda")
+    o4, l4 = torch.empty_like(q4), torch.empty(dc.B, dc.Hq, dc.Tq, device="cuda")
+    plan3 = fa.attn_fwd_plan(pc.B, pc.Hq, pc.Hkv, pc.Tq, pc.Tk, pc.d, pc.causal, fa.FATTN_BF16)
+    plan4 = fa.attn_fwd_plan(dc.B, dc.Hq, dc.Hkv, dc.Tq, dc.Tk, dc.d, dc.causal, fa.FATTN_BF16)
+
+    def step():
+        fa.attn_fwd(q3, k3, v3, causal=pc.causal, scale=pc.scale, out=o3, lse=l3)
+        fa.attn_fwd(q4, k4, v4, causal=dc.causal, scale=dc.scale, out=o4, lse=l4)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        fa.attn_fwd(q3, k3, v3, causal=pc.causal, scale=pc.scale, out=o3, lse=l3)
+        ev[i][1].record()
+        fa.attn_fwd(q4, k4, v4, causal=dc.causal, scale=dc.scale, out=o4, lse=l4)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prefill_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    decode_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    if not (bool(torch.isfinite(o3).all()) and bool(torch.isfinite(o4).all())):
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+
+    flops = prefill_flops(pc.B, pc.Hq, pc.Tq, pc.Tk, pc.d, pc.causal)
+    tflops = flops / (prefill_ms * 1e-3) / 1e12
+    dbytes = decode_bytes(dc.B, dc.Hq, dc.Hkv, dc.Tk, dc.d)
+    gbs = dbytes / (decode_ms * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_baseline == "auto":
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill bf16 B=1 H=32 T=8192 d=128 + GQA decode bf16 B=64 "
+                        "Hq=64 Hkv=8 Tq=1 Tk=8192 d=128",
+            "prefill_launch": plan3,
+            "decode_launch": plan4,
+            "inputs": "N(0,1) per-head seeded draws rounded to bf16, resident in HBM",
+        },
+        "prefill": {"ms": round(prefill_ms, 4), "tflops": round(tflops, 2),
+                    "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+                    "flops_per_call": flops},
+        "decode": {"ms": round(decode_ms, 4), "gbs": round(gbs, 1),
+                   "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                   "bytes_per_call": dbytes,
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                "traffic": traffic_for("decode_bf16.hip", "decode")}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for("prefill_bf16.hip", "prefill")},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

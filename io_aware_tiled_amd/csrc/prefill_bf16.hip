@@ -19,6 +19,15 @@
 //  * K and V tiles are double-buffered in LDS: the next tile's global loads are in flight in
 //    registers while the current tile is consumed, then written to the other LDS stage.
 //  * the exponentials run on the fp32 VALU as exp2 with log2(e) folded into the scale.
+//  * the reference maximum is re-based lazily: the exponent base only moves when a row's maximum
+//    grows by more than kRebase (log2 units), so the 64-register accumulator rescale is rare.
+//    Any reference gives the same O = acc / l and LSE = m + log l ("Efficient attention & KV
+//    cache", section 2.1: the max is there only for numerical safety); the weights stay below
+//    2^kRebase, far inside fp32 and bf16 range.
+//  * the row sum is taken from the bf16 weights the PV product uses (v_dot2 against ones), so the
+//    normaliser matches the weights exactly and costs half the adds.
+//  * K and V are read with buffer loads: rows past Tk come back as zeros from the hardware range
+//    check, so ragged tiles need no branches.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -29,12 +38,15 @@ namespace fattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kRebase = 8.0f;               // lazy re-base threshold, log2 units
+constexpr int kBufferFlags = 0x00020000;      // raw buffer, 32-bit data format
 
 template <int D, int BC, int NW>
 struct Shape {
@@ -60,11 +72,19 @@ __device__ __forceinline__ int vt_pos_of_group(int kg) {  // start of keys 4kg..
   return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
 }
 
+// Low halves of a and b as one word (a low), and the high halves likewise.
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Buffer resource for rows [row0, T) of a [T, D] bf16 slice: reads past T return zeros.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const __bf16* slice, int row0, int T) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(slice + (size_t)row0 * D),
+                                           (short)0, (T - row0) * D * 2, kBufferFlags);
 }
 
 // Two floats rounded to bf16 (nearest-even) and packed low/high.
@@ -83,7 +103,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int col = lane & 31;   // query row within the wave (MFMA column)
   const int hf = lane >> 5;    // half-wave
 
@@ -131,36 +151,32 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     qb8[kk] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  // ---- staging registers for the next tile
+  // ---- staging registers for the next tile; byte offsets within a tile are fixed per thread
   u32x4 kreg[S::K_PER];
   u32x4 vreg[S::V_PER][4];
+  int koff[S::K_PER], voff[S::V_PER];
+#pragma unroll
+  for (int i = 0; i < S::K_PER; ++i) koff[i] = (tid + i * S::NT) * 16;
+#pragma unroll
+  for (int i = 0; i < S::V_PER; ++i) {
+    const int it = tid + i * S::NT;
+    voff[i] = (4 * (it % (BC / 4))) * D * 2 + (it / (BC / 4)) * 16;
+  }
 
   auto load_tile = [&](int j0) {
+    const __amdgpu_buffer_rsrc_t kr = rows_rsrc<D>(Kh, j0, Tk);
+    const __amdgpu_buffer_rsrc_t vr = rows_rsrc<D>(Vh, j0, Tk);
 #pragma unroll
-    for (int i = 0; i < S::K_PER; ++i) {
-      const int c = tid + i * S::NT;
-      if (c < S::K_CHUNKS) {
-        const int row = c / (D / 8), cc = c % (D / 8);
-        const int key = j0 + row;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < Tk) x = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + cc * 8);
-        kreg[i] = x;
+    for (int i = 0; i < S::K_PER; ++i)
+      if (S::K_CHUNKS % S::NT == 0 || tid + i * S::NT < S::K_CHUNKS)
+        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0);
+#pragma unroll
+    for (int i = 0; i < S::V_PER; ++i)
+      if (S::V_ITEMS % S::NT == 0 || tid + i * S::NT < S::V_ITEMS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vreg[i][r] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i] + r * D * 2, 0, 0);
       }
-    }
-#pragma unroll
-    for (int i = 0; i < S::V_PER; ++i) {
-      const int it = tid + i * S::NT;
-      if (it < S::V_ITEMS) {
-        const int kg = it % (BC / 4), dg = it / (BC / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = j0 + 4 * kg + r;
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (key < Tk) x = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + dg * 8);
-          vreg[i][r] = x;
-        }
-      }
-    }
   };
 
   auto store_tile = [&](int stage) {
@@ -198,6 +214,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   // ---- running statistics (log2 domain: M = max of log2_scale * s over the keys seen)
   float M = kNegInf;
   float lsum = 0.f;  // this lane's share of the row sum (half of the keys of each tile)
+  // M is the exponent base of this lane's row, in log2 units of the scaled scores
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
@@ -215,18 +232,30 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
       const __bf16* Ks = lds + (j & 1) * S::STAGE;
       const __bf16* Vs = Ks + S::K_ELEMS;
 
-      // S^T tile: rows = keys (32 per MFMA tile), columns = this wave's 32 queries
+      // S^T tile: rows = keys (32 per MFMA tile), columns = this wave's 32 queries. The K
+      // operands of a 32-key half are all read from LDS before its MFMA chain starts, so the
+      // read latency is paid once per chain rather than once per MFMA.
       f32x16 s[BC / 32];
 #pragma unroll
       for (int t = 0; t < BC / 32; ++t) {
+        bf16x8 ka[D / 16];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+          ka[kk] = *reinterpret_cast<const bf16x8*>(Ks + (32 * t + col) * S::KS + 16 * kk + 8 * hf);
         s[t] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(Ks + (32 * t + col) * S::KS + 16 * kk + 8 * hf);
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb8[kk], s[t], 0, 0, 0);
-        }
+        for (int kk = 0; kk < D / 16; ++kk)
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qb8[kk], s[t], 0, 0, 0);
       }
+      // issue order: the first half's reads, then its MFMAs alternating with the second half's
+      // reads, then the second half's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+#pragma unroll
+      for (int i = 0; i < (BC / 32 - 1) * (D / 16); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
 
       // mask only on the diagonal and ragged tiles
       const bool need_mask = (j0 + BC > Tk) || (causal && j0 + BC - 1 > qw0 + off);
@@ -248,39 +277,43 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(M, mx * log2_scale);
-      const float base = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(M - base);  // 0 while M is -inf
-      M = m_new;
-
-      float psum = 0.f;
-      bf16x8 pb[BC / 16];
-#pragma unroll
-      for (int t = 0; t < BC / 32; ++t)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i], log2_scale, -base));
-            psum += p;
-            pb[2 * t + c2][i] = (__bf16)p;
-          }
-      lsum = fmaf(alpha, lsum, psum);
-
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      const float mt = mx * log2_scale;
+      const bool grow = mt > M + kRebase;  // always true on the first tile a row sees
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mt : M;
+        const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M is -inf
+        lsum *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+        M = m_new;
       }
+      const float base = (M == kNegInf) ? 0.f : M;
 
-      // O^T += V^T P^T over the tile's keys, 16 keys per MFMA
+      // Per 16-key chunk: weights exp2(s * log2_scale - base) <= 2^kRebase rounded to bf16 (the
+      // row sum adds exactly those bf16 weights), then O^T += V^T P^T for that chunk, so the
+      // chunk's MFMAs can run while the next chunk's exponentials are computed.
+      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+      for (int ch = 0; ch < BC / 16; ++ch) {
+        const int t = ch >> 1, c2 = ch & 1;
+        bf16x8 pb;
 #pragma unroll
-        for (int ch = 0; ch < BC / 16; ++ch) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(Vs + (32 * dt + col) * S::VS + 16 * ch + 8 * hf);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ch], acc[dt], 0, 0, 0);
+        for (int i = 0; i < 8; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i], log2_scale, -base));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i + 1], log2_scale, -base));
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+          pb[i] = pp[0];
+          pb[i + 1] = pp[1];
         }
+        bf16x8 va[D / 32];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          va[dt] = *reinterpret_cast<const bf16x8*>(Vs + (32 * dt + col) * S::VS + 16 * ch + 8 * hf);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], pb, acc[dt], 0, 0, 0);
+      }
     }
 
     if (j + 1 < ntiles) store_tile((j + 1) & 1);
