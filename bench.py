@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
 PREFILL = "c3_bf16_causal_t8192_d128"
 DECODE = "c4_bf16_gqa_decode_tk8192_d128"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def prefill_flops(B, H, Tq, Tk, d, causal):
@@ -70,18 +70,25 @@ def device_inputs(cfg, torch):
             build(inputs.V_ID, cfg.Hkv, cfg.Tk))
 
 
-def traffic_for(kernel_source, launches_key):
-    """HBM bytes per launch from the committed counter summary, or None if it is missing or the
-    kernel source changed since the counters were taken."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    ent = rec.get(launches_key)
-    if not ent or ent.get("source_sha256_16") != source_hash(kernel_source):
-        return None
-    return ent.get("hbm_bytes_per_launch")
+def traffic_for(kernel_source, key):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE counters, read from the
+    `traffic-record:` line of the committed profile summaries; None when no summary has it or
+    the kernel source changed since the counters were taken."""
+    import glob
+
+    want = source_hash(kernel_source)
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic-record:"):
+                    try:
+                        rec = json.loads(line.split(":", 1)[1])
+                    except ValueError:
+                        continue
+                    if (rec.get("key") == key and rec.get("source") == kernel_source
+                            and rec.get("source_sha256_16") == want):
+                        return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(budget_s=12.0, max_heads=32):
@@ -127,8 +134,9 @@ def calibrate_copy(nbytes, reps=3):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the clock ramps up over the first ~20 ms of back-to-back work; warm up past that
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-baseline", choices=["auto", "off"], default="auto")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
