@@ -67,7 +67,9 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
     tmp = LIB_PATH + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    # --no-undefined: a kernel whose host-side launch stub was not emitted fails here, not at load
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp]
+         + objs, verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -9,25 +9,27 @@
 //
 // Mapping onto CDNA4:
 //  * every wavefront owns 32 query rows; both products run on v_mfma_f32_32x32x16_bf16 with fp32
-//    accumulation. The scores are formed transposed, S^T = K Q^T, so a lane holds one query row
-//    (lane % 32) and 16 keys per 32x32 tile: the row max and row sum are in-lane except for one
-//    exchange between the two half-waves.
-//  * the output is accumulated transposed as well, O^T = V^T P^T. The P^T operand is the S^T
-//    accumulator itself converted to bf16 (no LDS round trip), because the MFMA reduction index
-//    may be any permutation of the keys as long as both operands use the same one; V is stored
-//    transposed in LDS in exactly that key order.
-//  * K and V tiles are double-buffered in LDS: the next tile's global loads are in flight in
-//    registers while the current tile is consumed, then written to the other LDS stage.
-//  * the exponentials run on the fp32 VALU as exp2 with log2(e) folded into the scale.
-//  * the reference maximum is re-based lazily: the exponent base only moves when a row's maximum
-//    grows by more than kRebase (log2 units), so the 64-register accumulator rescale is rare.
-//    Any reference gives the same O = acc / l and LSE = m + log l ("Efficient attention & KV
-//    cache", section 2.1: the max is there only for numerical safety); the weights stay below
-//    2^kRebase, far inside fp32 and bf16 range.
-//  * the row sum is taken from the bf16 weights the PV product uses (v_dot2 against ones), so the
-//    normaliser matches the weights exactly and costs half the adds.
-//  * K and V are read with buffer loads: rows past Tk come back as zeros from the hardware range
-//    check, so ragged tiles need no branches.
+//    accumulation. Scores are formed transposed, S^T = K Q^T, so a lane holds one query row
+//    (lane % 32) and 16 keys per 32x32 tile: row max and row sum are in-lane except for one
+//    exchange between the half-waves (v_permlane32_swap).
+//  * the output is accumulated transposed too, O^T = V^T P^T. The P^T operand is the S^T
+//    accumulator converted to bf16 in place; the MFMA reduction index may be any permutation of
+//    the keys as long as both operands use it, and the V^T operand is assembled in that key order
+//    by LDS transpose reads (ds_read_b64_tr_b16) from V stored row-major.
+//  * K and V tiles travel global -> LDS by direct-to-LDS buffer loads (no registers, no LDS store
+//    instructions), two stages each, with K one tile ahead of V. Rows are stored with their
+//    16-byte chunks XOR-swizzled so both the K operand reads and the transpose reads of V are
+//    free of bank conflicts. Rows past Tk come back as zeros from the buffer range check.
+//  * software pipeline: while the exponentials of tile j run on the VALU, the matrix cores
+//    compute the scores of tile j+1; while the PV products of tile j run, the VALU takes the row
+//    maxima of tile j+1. Tiles that need a mask (causal diagonal, ragged end) take a separate,
+//    non-interleaved path.
+//  * exponentials are exp2 with log2(e) folded into the scale. The exponent base moves lazily:
+//    only when a row's maximum exceeds it by more than kRebase (log2 units) are l and the
+//    accumulator rescaled. Any base gives the same O = acc / l and LSE = base + log l
+//    ("Efficient attention & KV cache", section 2.1: the max is there only for numerical
+//    safety); weights stay below 2^kRebase.
+//  * the row sum adds the bf16 weights the PV product uses (v_dot2 against ones).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -39,52 +41,82 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kRebase = 8.0f;               // lazy re-base threshold, log2 units
-constexpr int kBufferFlags = 0x00020000;      // raw buffer, 32-bit data format
+constexpr float kRebase = 8.0f;           // lazy re-base threshold, log2 units
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 template <int D, int BC, int NW>
 struct Shape {
-  static constexpr int BR = 32 * NW;       // query rows per workgroup
-  static constexpr int NT = 64 * NW;       // threads per workgroup
-  static constexpr int KS = D + 8;         // LDS row pitch of K (elements): +16 bytes
-  static constexpr int VS = BC + 8;        // LDS row pitch of V^T (elements): +16 bytes
-  static constexpr int K_ELEMS = BC * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int K_CHUNKS = BC * D / 8;           // 16-byte pieces of a K tile
-  static constexpr int K_PER = (K_CHUNKS + NT - 1) / NT;
-  static constexpr int V_ITEMS = (BC / 4) * (D / 8);    // 4 keys x 8 dims per item
-  static constexpr int V_PER = (V_ITEMS + NT - 1) / NT;
-  static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
+  static constexpr int BR = 32 * NW;               // query rows per workgroup
+  static constexpr int NT = 64 * NW;               // threads per workgroup
+  static constexpr int RB = 2 * D;                 // bytes per K or V row
+  static constexpr int C = D / 8;                  // 16-byte chunks per row
+  static constexpr int R256 = RB >= 256 ? 1 : 256 / RB;  // rows per 256 bytes
+  static constexpr int G = C / 4;
+  static constexpr int TILE = BC * RB;             // bytes per K or V tile
+  static constexpr int NI = TILE / 1024;           // direct-to-LDS loads (1 KB each) per tile
+  static constexpr int NI_W = (NI + NW - 1) / NW;  // per wave
+  static constexpr int RPI = 1024 / RB;            // rows per direct-to-LDS load
+  static constexpr int K_OFF = 0;                  // LDS: K stage 0, K stage 1, V stage 0, V stage 1
+  static constexpr int V_OFF = 2 * TILE;
+  static constexpr int LDS_BYTES = 4 * TILE;
+  static_assert(D % 32 == 0 && D <= 128 && BC % 32 == 0 && TILE % 1024 == 0, "tile shape");
 };
 
-// Position of tile-local key k inside a V^T row. Within each group of 16 keys the order is
-// {0-3, 8-11, 4-7, 12-15}: that is the order in which one half-wave holds its eight keys of a
-// 16-key chunk in the S^T accumulator (rows 4h..4h+3 and 8+4h..8+4h+3 for half h).
-__device__ __forceinline__ int vt_pos_of_group(int kg) {  // start of keys 4kg..4kg+3
-  return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+// Chunk swizzle of row r: a bijection on the chunk index so that 16 consecutive rows read at the
+// same logical chunk, and the four rows a transpose read takes at once, hit distinct banks.
+template <int D, int BC, int NW>
+__device__ __forceinline__ int swz(int r) {
+  using S = Shape<D, BC, NW>;
+  const int u = (r / S::R256) % S::C;
+  return 4 * (u % S::G) + (u / S::G) % 4;
 }
-
-// Low halves of a and b as one word (a low), and the high halves likewise.
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+// Byte offset of row r inside a tile; logical chunk c of that row is at rowbase(r) ^ (c << 4).
+template <int D, int BC, int NW>
+__device__ __forceinline__ int rowbase(int r) {
+  using S = Shape<D, BC, NW>;
+  return r * S::RB + (swz<D, BC, NW>(r) << 4);
 }
 
 // Buffer resource for rows [row0, T) of a [T, D] bf16 slice: reads past T return zeros.
 template <int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const __bf16* slice, int row0, int T) {
+  const int rows = T - row0;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(slice + (size_t)row0 * D),
-                                           (short)0, (T - row0) * D * 2, kBufferFlags);
+                                           (short)0, rows > 0 ? rows * D * 2 : 0, kBufferFlags);
+}
+
+// One K or V tile, global -> LDS by direct-to-LDS loads: this wave's share of the 1 KB loads.
+// (A device function rather than a lambda: the builtin exists only in the device pass.)
+template <int D, int BC, int NW>
+__device__ __forceinline__ void dma_tile(const __bf16* head, int j0, int Tk, unsigned char* lds,
+                                         int lds_off, int wave, const int (&dvo)[Shape<D, BC, NW>::NI_W]) {
+  using S = Shape<D, BC, NW>;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(head, j0, Tk);
+#pragma unroll
+  for (int i = 0; i < S::NI_W; ++i) {
+    const int q = wave + i * NW;
+    if (S::NI % NW == 0 || q < S::NI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + lds_off + q * 1024), 16,
+                                               dvo[i], 0, 0, 0);
+  }
+}
+
+// Values of lane l and lane l ^ 32 (the same query row in the other half-wave), via
+// v_permlane32_swap on two copies of x. Written as inline asm because the compiler folds the
+// two results of the builtin into one when both inputs are the same value.
+__device__ __forceinline__ void halves(float x, float& lo_half, float& hi_half) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo_half = __builtin_bit_cast(float, a);  // lanes 0-31: own; lanes 32-63: lane - 32
+  hi_half = __builtin_bit_cast(float, b);  // lanes 0-31: lane + 32; lanes 32-63: own
 }
 
 // Two floats rounded to bf16 (nearest-even) and packed low/high.
@@ -99,7 +131,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     __bf16* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Tq, int Tk,
     int causal, float log2_scale, int qsign, int schedule) {
   using S = Shape<D, BC, NW>;
-  extern __shared__ __align__(16) __bf16 lds[];
+  extern __shared__ __align__(1024) unsigned char lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,6 +166,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   const int q_end = min(i0 + S::BR, Tq);
   const int kv_end = causal ? min(Tk, q_end + off) : Tk;
   const int ntiles = (kv_end + BC - 1) / BC;
+  // tiles [0, jm) need no mask for any row of the workgroup
+  int jm = Tk / BC;
+  if (causal) jm = min(jm, (i0 + off + 1) / BC);
+  jm = min(jm, ntiles);
 
   // ---- this wave's query rows; Q^T operand held in registers for the whole loop
   const int qw0 = i0 + 32 * wave;
@@ -151,178 +187,186 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     qb8[kk] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  // ---- staging registers for the next tile; byte offsets within a tile are fixed per thread
-  u32x4 kreg[S::K_PER];
-  u32x4 vreg[S::V_PER][4];
-  int koff[S::K_PER], voff[S::V_PER];
+  // ---- per-lane constant offsets
+  // direct-to-LDS loads: LDS slot `lane` of load q holds row q*RPI + lane/C, physical chunk
+  // lane%C, i.e. logical chunk (lane%C) ^ swz(row) of that row
+  int dvo[S::NI_W];
 #pragma unroll
-  for (int i = 0; i < S::K_PER; ++i) koff[i] = (tid + i * S::NT) * 16;
-#pragma unroll
-  for (int i = 0; i < S::V_PER; ++i) {
-    const int it = tid + i * S::NT;
-    voff[i] = (4 * (it % (BC / 4))) * D * 2 + (it / (BC / 4)) * 16;
+  for (int i = 0; i < S::NI_W; ++i) {
+    const int q = wave + i * NW;
+    const int r = q * S::RPI + lane / S::C;
+    dvo[i] = r * S::RB + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
   }
+  // K operand of row col, chunk 2kk+hf: ka ^ (kk << 5), plus 32t rows for the t-th key half
+  const int ka = rowbase<D, BC, NW>(col) ^ (hf << 4);
+  // V^T operand by transpose reads: lane = 16*(2*vq + vg) + 4*ve + va reads 4 d-values starting
+  // at 32*dt + 16*vg + 4*va of key row 16*ch + 8*rr + 4*vq + ve (rr = 0, 1 for the two reads)
+  const int vq = lane >> 5, vg = (lane >> 4) & 1, ve = (lane >> 2) & 3, va = lane & 3;
+  int vab[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr)
+    vab[rr] = (rowbase<D, BC, NW>(8 * rr + 4 * vq + ve) ^ ((2 * vg + (va >> 1)) << 4)) + 8 * (va & 1);
 
-  auto load_tile = [&](int j0) {
-    const __amdgpu_buffer_rsrc_t kr = rows_rsrc<D>(Kh, j0, Tk);
-    const __amdgpu_buffer_rsrc_t vr = rows_rsrc<D>(Vh, j0, Tk);
-#pragma unroll
-    for (int i = 0; i < S::K_PER; ++i)
-      if (S::K_CHUNKS % S::NT == 0 || tid + i * S::NT < S::K_CHUNKS)
-        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, koff[i], 0, 0);
-#pragma unroll
-    for (int i = 0; i < S::V_PER; ++i)
-      if (S::V_ITEMS % S::NT == 0 || tid + i * S::NT < S::V_ITEMS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          vreg[i][r] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[i] + r * D * 2, 0, 0);
-      }
+  auto issue_tile = [&](const __bf16* head, int j0, int lds_off) {
+    dma_tile<D, BC, NW>(head, j0, Tk, lds, lds_off, wave, dvo);
   };
 
-  auto store_tile = [&](int stage) {
-    __bf16* Ks = lds + stage * S::STAGE;
-    __bf16* Vs = Ks + S::K_ELEMS;
+  // S^T for one tile from a K stage
+  auto qk = [&](f32x16 (&s)[BC / 32], int kst) {
 #pragma unroll
-    for (int i = 0; i < S::K_PER; ++i) {
-      const int c = tid + i * S::NT;
-      if (c < S::K_CHUNKS) {
-        const int row = c / (D / 8), cc = c % (D / 8);
-        *reinterpret_cast<u32x4*>(Ks + row * S::KS + cc * 8) = kreg[i];
-      }
-    }
+    for (int t = 0; t < BC / 32; ++t) {
+      s[t] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < S::V_PER; ++i) {
-      const int it = tid + i * S::NT;
-      if (it < S::V_ITEMS) {
-        const int kg = it % (BC / 4), dg = it / (BC / 4);
-        const int pos = vt_pos_of_group(kg);
-        // 4 keys x 8 dims -> 8 rows of V^T, 4 consecutive key positions each
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a0 = vreg[i][0][w], a1 = vreg[i][1][w];
-          const uint32_t a2 = vreg[i][2][w], a3 = vreg[i][3][w];
-          u32x2 even = {pack_lo(a0, a1), pack_lo(a2, a3)};
-          u32x2 odd = {pack_hi(a0, a1), pack_hi(a2, a3)};
-          const int d = 8 * dg + 2 * w;
-          *reinterpret_cast<u32x2*>(Vs + d * S::VS + pos) = even;
-          *reinterpret_cast<u32x2*>(Vs + (d + 1) * S::VS + pos) = odd;
-        }
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = *(const LDS_AS bf16x8*)(lds + kst + ((ka ^ (kk << 5)) + 32 * t * S::RB));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb8[kk], s[t], 0, 0, 0);
       }
     }
   };
 
-  // ---- running statistics (log2 domain: M = max of log2_scale * s over the keys seen)
+  auto mask_tile = [&](f32x16 (&s)[BC / 32], int j0) {
+    const int last = causal ? min(Tk - 1, qrow + off) : Tk - 1;
+#pragma unroll
+    for (int t = 0; t < BC / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (key > last) s[t][r] = kNegInf;
+      }
+  };
+
+  // ---- running state (M: exponent base of this lane's row, log2 units of the scaled scores)
   float M = kNegInf;
   float lsum = 0.f;  // this lane's share of the row sum (half of the keys of each tile)
-  // M is the exponent base of this lane's row, in log2 units of the scaled scores
   f32x16 acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // row maximum of a score tile and the lazy re-base of the running state
+  auto rebase = [&](f32x16 (&s)[BC / 32]) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < BC / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    float m_lo, m_hi;
+    halves(mx, m_lo, m_hi);
+    mx = fmaxf(m_lo, m_hi);
+    const float mt = mx * log2_scale;
+    const bool grow = mt > M + kRebase;  // always true on the first tile a row sees
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : M;
+      const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M is -inf
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
+      M = m_new;
+    }
+  };
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int j0 = j * BC;
-    if (j + 1 < ntiles) load_tile(j0 + BC);
-
-    const bool active = wave_has_rows && (!causal || j0 <= wave_last + off);
-    if (active) {
-      const __bf16* Ks = lds + (j & 1) * S::STAGE;
-      const __bf16* Vs = Ks + S::K_ELEMS;
-
-      // S^T tile: rows = keys (32 per MFMA tile), columns = this wave's 32 queries. The K
-      // operands of a 32-key half are all read from LDS before its MFMA chain starts, so the
-      // read latency is paid once per chain rather than once per MFMA.
-      f32x16 s[BC / 32];
+  // weights of a score tile (bf16) and their row sum
+  auto weights = [&](f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 16]) {
+    const float base = (M == kNegInf) ? 0.f : M;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-      for (int t = 0; t < BC / 32; ++t) {
-        bf16x8 ka[D / 16];
+    for (int ch = 0; ch < BC / 16; ++ch) {
+      const int t = ch >> 1, c2 = ch & 1;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          ka[kk] = *reinterpret_cast<const bf16x8*>(Ks + (32 * t + col) * S::KS + 16 * kk + 8 * hf);
-        s[t] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qb8[kk], s[t], 0, 0, 0);
-      }
-      // issue order: the first half's reads, then its MFMAs alternating with the second half's
-      // reads, then the second half's MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
-#pragma unroll
-      for (int i = 0; i < (BC / 32 - 1) * (D / 16); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
-
-      // mask only on the diagonal and ragged tiles
-      const bool need_mask = (j0 + BC > Tk) || (causal && j0 + BC - 1 > qw0 + off);
-      if (need_mask) {
-        const int last = causal ? min(Tk - 1, qrow + off) : Tk - 1;
-#pragma unroll
-        for (int t = 0; t < BC / 32; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (key > last) s[t][r] = kNegInf;
-          }
-      }
-
-      // online softmax update for this lane's query row
-      float mx = kNegInf;
-#pragma unroll
-      for (int t = 0; t < BC / 32; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = mx * log2_scale;
-      const bool grow = mt > M + kRebase;  // always true on the first tile a row sees
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? mt : M;
-        const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M is -inf
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
-        M = m_new;
-      }
-      const float base = (M == kNegInf) ? 0.f : M;
-
-      // Per 16-key chunk: weights exp2(s * log2_scale - base) <= 2^kRebase rounded to bf16 (the
-      // row sum adds exactly those bf16 weights), then O^T += V^T P^T for that chunk, so the
-      // chunk's MFMAs can run while the next chunk's exponentials are computed.
-      const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-      for (int ch = 0; ch < BC / 16; ++ch) {
-        const int t = ch >> 1, c2 = ch & 1;
-        bf16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i], log2_scale, -base));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i + 1], log2_scale, -base));
-          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-          pb[i] = pp[0];
-          pb[i + 1] = pp[1];
-        }
-        bf16x8 va[D / 32];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          va[dt] = *reinterpret_cast<const bf16x8*>(Vs + (32 * dt + col) * S::VS + 16 * ch + 8 * hf);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], pb, acc[dt], 0, 0, 0);
+      for (int i = 0; i < 8; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i], log2_scale, -base));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i + 1], log2_scale, -base));
+        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+        pb[ch][i] = pp[0];
+        pb[ch][i + 1] = pp[1];
       }
     }
+  };
 
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
+  // O^T += V^T P^T for one tile from a V stage
+  auto pv = [&](const bf16x8 (&pb)[BC / 16], int vst) {
+#pragma unroll
+    for (int ch = 0; ch < BC / 16; ++ch)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(lds + vst + ((vab[0] ^ (dt << 6)) + 16 * ch * S::RB)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(lds + vst + ((vab[1] ^ (dt << 6)) + 16 * ch * S::RB)));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ch], acc[dt], 0, 0, 0);
+      }
+  };
+
+  auto active = [&](int j) { return wave_has_rows && (!causal || j * BC <= wave_last + off); };
+
+  // ---- prologue: clear the V stages (rows past Tk must never hold non-finite leftovers), then
+  // load K(0), V(0), K(1); scores, mask and maximum of tile 0
+  for (int i = tid; i < 2 * S::TILE / 16; i += S::NT)
+    *(LDS_AS u32x4*)(lds + S::V_OFF + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  issue_tile(Kh, 0, S::K_OFF);
+  issue_tile(Vh, 0, S::V_OFF);
+  issue_tile(Kh, BC, S::K_OFF + S::TILE);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 sa[BC / 32], sb[BC / 32];
+  if (active(0)) {
+    qk(sa, S::K_OFF);
+    if (jm == 0) mask_tile(sa, 0);
+    rebase(sa);
+  }
+  __syncthreads();
+
+  // ---- steady state: tiles j and j+1 both unmasked and every wave active. Unrolled by two so
+  // the score buffers and LDS stages alternate without copies.
+  auto fast_step = [&](f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32], int j, int par) {
+    const int j0 = j * BC;
+    issue_tile(Vh, j0 + BC, S::V_OFF + (1 - par) * S::TILE);
+    issue_tile(Kh, j0 + 2 * BC, S::K_OFF + par * S::TILE);
+    bf16x8 pb[BC / 16];
+    qk(sn, S::K_OFF + (1 - par) * S::TILE);
+    weights(sc, pb);
+    pv(pb, S::V_OFF + par * S::TILE);
+    rebase(sn);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 2 < jm; j += 2) {
+    fast_step(sa, sb, j, 0);
+    fast_step(sb, sa, j + 1, 1);
+  }
+
+  // ---- remaining tiles: masks, inactive waves and the end of the pipeline
+  for (; j < ntiles; ++j) {
+    const int j0 = j * BC;
+    const int par = j & 1;
+    issue_tile(Vh, j0 + BC, S::V_OFF + (1 - par) * S::TILE);
+    issue_tile(Kh, j0 + 2 * BC, S::K_OFF + par * S::TILE);
+    const bool act_next = (j + 1 < ntiles) && active(j + 1);
+    if (act_next) {
+      qk(sb, S::K_OFF + (1 - par) * S::TILE);
+      if (j + 1 >= jm) mask_tile(sb, j0 + BC);
+    }
+    if (active(j)) {
+      bf16x8 pb[BC / 16];
+      weights(sa, pb);
+      pv(pb, S::V_OFF + par * S::TILE);
+    }
+    if (act_next) rebase(sb);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < BC / 32; ++t) sa[t] = sb[t];
   }
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (M + log2 l)
   if (!wave_has_rows) return;
-  const float l = lsum + __shfl_xor(lsum, 32);
+  float l_lo, l_hi;
+  halves(lsum, l_lo, l_hi);
+  const float l = l_lo + l_hi;
   if (qrow >= Tq) return;
   const float inv = 1.f / l;
   __bf16* Orow = O + (((size_t)b * Hq + h) * (size_t)Tq + qrow) * D;
