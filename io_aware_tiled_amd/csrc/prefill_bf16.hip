@@ -64,9 +64,7 @@ struct Shape {
   static constexpr int NI = TILE / 1024;           // direct-to-LDS loads (1 KB each) per tile
   static constexpr int NI_W = (NI + NW - 1) / NW;  // per wave
   static constexpr int RPI = 1024 / RB;            // rows per direct-to-LDS load
-  static constexpr int K_OFF = 0;                  // LDS: K stage 0, K stage 1, V stage 0, V stage 1
-  static constexpr int V_OFF = 2 * TILE;
-  static constexpr int LDS_BYTES = 4 * TILE;
+  static constexpr int LDS_BYTES = 4 * TILE;       // K and V, two stages each
   static_assert(D % 32 == 0 && D <= 128 && BC % 32 == 0 && TILE % 1024 == 0, "tile shape");
 };
 
@@ -96,16 +94,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const __bf16* slice,
 // One K or V tile, global -> LDS by direct-to-LDS loads: this wave's share of the 1 KB loads.
 // (A device function rather than a lambda: the builtin exists only in the device pass.)
 template <int D, int BC, int NW>
-__device__ __forceinline__ void dma_tile(const __bf16* head, int j0, int Tk, unsigned char* lds,
-                                         int lds_off, int wave, const int (&dvo)[Shape<D, BC, NW>::NI_W]) {
+__device__ __forceinline__ void dma_tile(const __bf16* head, int j0, int Tk, unsigned char* dst,
+                                         int wave, const int (&dvo)[Shape<D, BC, NW>::NI_W]) {
   using S = Shape<D, BC, NW>;
   const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(head, j0, Tk);
 #pragma unroll
   for (int i = 0; i < S::NI_W; ++i) {
     const int q = wave + i * NW;
     if (S::NI % NW == 0 || q < S::NI)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lds + lds_off + q * 1024), 16,
-                                               dvo[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + q * 1024), 16, dvo[i], 0,
+                                               0, 0);
   }
 }
 
@@ -131,7 +129,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     __bf16* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Tq, int Tk,
     int causal, float log2_scale, int qsign, int schedule) {
   using S = Shape<D, BC, NW>;
-  extern __shared__ __align__(1024) unsigned char lds[];
+  // One array per stage, so the compiler can tell a direct-to-LDS load into one stage from reads
+  // of another and does not make those reads wait for the load.
+  __shared__ __align__(1024) unsigned char k_st0[S::TILE], k_st1[S::TILE];
+  __shared__ __align__(1024) unsigned char v_st0[S::TILE], v_st1[S::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -207,18 +208,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   for (int rr = 0; rr < 2; ++rr)
     vab[rr] = (rowbase<D, BC, NW>(8 * rr + 4 * vq + ve) ^ ((2 * vg + (va >> 1)) << 4)) + 8 * (va & 1);
 
-  auto issue_tile = [&](const __bf16* head, int j0, int lds_off) {
-    dma_tile<D, BC, NW>(head, j0, Tk, lds, lds_off, wave, dvo);
+  auto issue_tile = [&](const __bf16* head, int j0, unsigned char* dst) {
+    dma_tile<D, BC, NW>(head, j0, Tk, dst, wave, dvo);
   };
 
   // S^T for one tile from a K stage
-  auto qk = [&](f32x16 (&s)[BC / 32], int kst) {
+  auto qk = [&](f32x16 (&s)[BC / 32], const unsigned char* kst) {
 #pragma unroll
     for (int t = 0; t < BC / 32; ++t) {
       s[t] = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 a = *(const LDS_AS bf16x8*)(lds + kst + ((ka ^ (kk << 5)) + 32 * t * S::RB));
+        const bf16x8 a = *(const LDS_AS bf16x8*)(kst + ((ka ^ (kk << 5)) + 32 * t * S::RB));
         s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb8[kk], s[t], 0, 0, 0);
       }
     }
@@ -284,15 +285,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   };
 
   // O^T += V^T P^T for one tile from a V stage
-  auto pv = [&](const bf16x8 (&pb)[BC / 16], int vst) {
+  auto pv = [&](const bf16x8 (&pb)[BC / 16], const unsigned char* vst) {
 #pragma unroll
     for (int ch = 0; ch < BC / 16; ++ch)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(lds + vst + ((vab[0] ^ (dt << 6)) + 16 * ch * S::RB)));
+            (LDS_AS i16x4*)(vst + ((vab[0] ^ (dt << 6)) + 16 * ch * S::RB)));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_AS i16x4*)(lds + vst + ((vab[1] ^ (dt << 6)) + 16 * ch * S::RB)));
+            (LDS_AS i16x4*)(vst + ((vab[1] ^ (dt << 6)) + 16 * ch * S::RB)));
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ch], acc[dt], 0, 0, 0);
@@ -303,17 +304,19 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
 
   // ---- prologue: clear the V stages (rows past Tk must never hold non-finite leftovers), then
   // load K(0), V(0), K(1); scores, mask and maximum of tile 0
-  for (int i = tid; i < 2 * S::TILE / 16; i += S::NT)
-    *(LDS_AS u32x4*)(lds + S::V_OFF + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  for (int i = tid; i < S::TILE / 16; i += S::NT) {
+    *(LDS_AS u32x4*)(v_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    *(LDS_AS u32x4*)(v_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  }
   __syncthreads();
-  issue_tile(Kh, 0, S::K_OFF);
-  issue_tile(Vh, 0, S::V_OFF);
-  issue_tile(Kh, BC, S::K_OFF + S::TILE);
+  issue_tile(Kh, 0, k_st0);
+  issue_tile(Vh, 0, v_st0);
+  issue_tile(Kh, BC, k_st1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sa[BC / 32], sb[BC / 32];
   if (active(0)) {
-    qk(sa, S::K_OFF);
+    qk(sa, k_st0);
     if (jm == 0) mask_tile(sa, 0);
     rebase(sa);
   }
@@ -321,39 +324,43 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
 
   // ---- steady state: tiles j and j+1 both unmasked and every wave active. Unrolled by two so
   // the score buffers and LDS stages alternate without copies.
-  auto fast_step = [&](f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32], int j, int par) {
+  auto fast_step = [&](f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32], int j, unsigned char* k_cur,
+                       unsigned char* k_nxt, unsigned char* v_cur, unsigned char* v_nxt) {
     const int j0 = j * BC;
-    issue_tile(Vh, j0 + BC, S::V_OFF + (1 - par) * S::TILE);
-    issue_tile(Kh, j0 + 2 * BC, S::K_OFF + par * S::TILE);
+    issue_tile(Vh, j0 + BC, v_nxt);
+    issue_tile(Kh, j0 + 2 * BC, k_cur);
     bf16x8 pb[BC / 16];
-    qk(sn, S::K_OFF + (1 - par) * S::TILE);
+    qk(sn, k_nxt);
     weights(sc, pb);
-    pv(pb, S::V_OFF + par * S::TILE);
+    pv(pb, v_cur);
     rebase(sn);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
   int j = 0;
   for (; j + 2 < jm; j += 2) {
-    fast_step(sa, sb, j, 0);
-    fast_step(sb, sa, j + 1, 1);
+    fast_step(sa, sb, j, k_st0, k_st1, v_st0, v_st1);
+    fast_step(sb, sa, j + 1, k_st1, k_st0, v_st1, v_st0);
   }
 
   // ---- remaining tiles: masks, inactive waves and the end of the pipeline
   for (; j < ntiles; ++j) {
     const int j0 = j * BC;
-    const int par = j & 1;
-    issue_tile(Vh, j0 + BC, S::V_OFF + (1 - par) * S::TILE);
-    issue_tile(Kh, j0 + 2 * BC, S::K_OFF + par * S::TILE);
+    unsigned char* k_cur = (j & 1) ? k_st1 : k_st0;
+    unsigned char* k_nxt = (j & 1) ? k_st0 : k_st1;
+    unsigned char* v_cur = (j & 1) ? v_st1 : v_st0;
+    unsigned char* v_nxt = (j & 1) ? v_st0 : v_st1;
+    issue_tile(Vh, j0 + BC, v_nxt);
+    issue_tile(Kh, j0 + 2 * BC, k_cur);
     const bool act_next = (j + 1 < ntiles) && active(j + 1);
     if (act_next) {
-      qk(sb, S::K_OFF + (1 - par) * S::TILE);
+      qk(sb, k_nxt);
       if (j + 1 >= jm) mask_tile(sb, j0 + BC);
     }
     if (active(j)) {
       bf16x8 pb[BC / 16];
       weights(sa, pb);
-      pv(pb, S::V_OFF + par * S::TILE);
+      pv(pb, v_cur);
     }
     if (act_next) rebase(sb);
     __builtin_amdgcn_s_waitcnt(0);
@@ -391,8 +398,8 @@ hipError_t launch_t(const Problem& p, int schedule, hipStream_t stream) {
   const long long grid = (long long)p.B * p.Hq * nqb;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, NW>), dim3((unsigned)grid), dim3(S::NT),
-                     S::LDS_BYTES, stream, static_cast<const __bf16*>(p.Q),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, NW>), dim3((unsigned)grid), dim3(S::NT), 0,
+                     stream, static_cast<const __bf16*>(p.Q),
                      static_cast<const __bf16*>(p.K), static_cast<const __bf16*>(p.V),
                      static_cast<__bf16*>(p.O), p.LSE, p.B, p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
                      p.log2_scale, p.qsign, schedule);
