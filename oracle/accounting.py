@@ -20,18 +20,37 @@ def attention_flops(B: int, H: int, Tq: int, Tk: int, d: int, causal: bool) -> f
     return f / 2.0 if causal else f
 
 
-def visible_pairs(Tq: int, Tk: int, causal: bool) -> int:
-    """Number of (query, key) pairs a mask leaves visible (bottom-right causal alignment)."""
+def visible_pairs(Tq: int, Tk: int, causal: bool, window: int = 0) -> int:
+    """Number of (query, key) pairs a mask leaves visible (bottom-right causal alignment).
+
+    ``window`` > 0 (causal only) keeps the last ``window`` positions of each row.
+    """
     if not causal:
         return Tq * Tk
     off = Tk - Tq
-    # row i sees min(Tk, i + off + 1) keys
-    return sum(min(Tk, i + off + 1) for i in range(Tq))
+    # row i sees keys 0..i+off, or only the last `window` of them
+    n = 0
+    for i in range(Tq):
+        seen = min(Tk, i + off + 1)
+        n += min(seen, window) if window > 0 else seen
+    return n
 
 
-def attention_flops_exact(B: int, H: int, Tq: int, Tk: int, d: int, causal: bool) -> float:
+def attention_flops_exact(B: int, H: int, Tq: int, Tk: int, d: int, causal: bool,
+                          window: int = 0) -> float:
     """4 d FLOPs for every visible (query, key) pair: the work a perfect mask skip leaves."""
-    return 4.0 * d * B * H * visible_pairs(Tq, Tk, causal)
+    return 4.0 * d * B * H * visible_pairs(Tq, Tk, causal, window)
+
+
+def window_cache_bytes(layers: int, kv_heads: int, head_dim: int, window: int,
+                       dtype_bytes: int = 2) -> int:
+    """KV-cache bytes of one sequence under a rolling window of ``window`` positions.
+
+    Per token and layer the cache holds one key and one value vector per kv head; a rolling
+    window caps the tokens held ("Efficient attention & KV cache", section 2.3 and exercise 1
+    of section 7).
+    """
+    return 2 * layers * kv_heads * head_dim * dtype_bytes * window
 
 
 def attention_bytes(B: int, H: int, T: int, d: int, dtype_bytes: int = 2) -> int:

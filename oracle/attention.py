@@ -11,6 +11,10 @@ Conventions (the readings of the pages that the GPU library follows too):
     and sees keys j <= i + Tk - Tq. For Tq == Tk this is the usual lower triangle used on every
     page; for Tq == 1 it sees every key, as a decode step over a KV cache does
     ("Efficient attention & KV cache", section 1);
+  * a sliding window of width W keeps, of the causal keys, only the last W positions: query i
+    at position p = i + Tk - Tq sees keys p - W < j <= p (exercise 4 of "4.2 FlashAttention I";
+    exercise 2 of "Efficient attention & KV cache", section 7). A window implies causal; W >= p+1
+    for every row is plain causal attention;
   * LSE is the natural log-sum-exp of the scaled, masked scores of a row: m + log(l)
     ("4.2 FlashAttention I", FlashAttention forward section; "Efficient attention & KV cache",
     section 3).
@@ -32,12 +36,22 @@ def _default_scale(d: int, scale: Optional[float]) -> float:
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+def _check_window(causal: bool, window: Optional[int]) -> None:
+    if window is None:
+        return
+    if not causal:
+        raise ValueError("a sliding window is a causal mask: pass causal=True")
+    if int(window) < 1:
+        raise ValueError("window must be >= 1")
+
+
 # --------------------------------------------------------------------------------------------
 # The definition, materialising S and P.
 # --------------------------------------------------------------------------------------------
 
 def dense_head(q, k, v, causal: bool, scale: Optional[float] = None,
-               rows: Optional[Sequence[int]] = None, return_p: bool = False):
+               rows: Optional[Sequence[int]] = None, return_p: bool = False,
+               window: Optional[int] = None):
     """Exact attention for one head, with the full score and probability rows materialised.
 
     Follows the reference attention of "4.2 FlashAttention I" (sections "The memory bottleneck"
@@ -48,8 +62,11 @@ def dense_head(q, k, v, causal: bool, scale: Optional[float] = None,
 
     q: [Tq, d]; k, v: [Tk, d]. ``rows`` restricts the computation to those query rows (their
     positions are still their indices in 0..Tq-1), which is how single outputs of a large problem
-    are checked one by one. Returns (O [n, d], LSE [n]) and P [n, Tk] when ``return_p``.
+    are checked one by one. ``window`` (with ``causal``) also hides keys at or before p - W, the
+    materialised reference of exercise 4 of "4.2 FlashAttention I". Returns (O [n, d],
+    LSE [n]) and P [n, Tk] when ``return_p``.
     """
+    _check_window(causal, window)
     q, k, v = _f64(q), _f64(k), _f64(v)
     Tq, d = q.shape
     Tk = k.shape[0]
@@ -60,7 +77,11 @@ def dense_head(q, k, v, causal: bool, scale: Optional[float] = None,
     S = sc * (q[idx] @ k.T)                                   # [n, Tk]
     if causal:
         off = Tk - Tq
-        hidden = np.arange(Tk)[None, :] > (idx[:, None] + off)
+        cols = np.arange(Tk)[None, :]
+        pos = idx[:, None] + off
+        hidden = cols > pos
+        if window is not None:
+            hidden = hidden | (cols <= pos - int(window))
         S = np.where(hidden, -np.inf, S)
     m = S.max(axis=1, keepdims=True)
     E = np.exp(S - m)
@@ -79,7 +100,8 @@ def _kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def dense_attention(Q, K, V, causal: bool, scale: Optional[float] = None):
+def dense_attention(Q, K, V, causal: bool, scale: Optional[float] = None,
+                    window: Optional[int] = None):
     """The definition over a whole [B, Hq, Tq, d] problem, head by head (float64).
 
     Returns O [B, Hq, Tq, d] and LSE [B, Hq, Tq].
@@ -92,29 +114,33 @@ def dense_attention(Q, K, V, causal: bool, scale: Optional[float] = None):
     for b in range(B):
         for h in range(Hq):
             g = _kv_head(h, Hq, Hkv)
-            O[b, h], L[b, h] = dense_head(Q[b, h], K[b, g], V[b, g], causal, scale)
+            O[b, h], L[b, h] = dense_head(Q[b, h], K[b, g], V[b, g], causal, scale,
+                                          window=window)
     return O, L
 
 
 def brute_attention(q, k, v, causal: bool, scale: Optional[float] = None,
-                    subtract_max: bool = True):
+                    subtract_max: bool = True, window: Optional[int] = None):
     """Scalar pure-Python attention for tiny inputs (lists of rows), one row at a time.
 
     The same computation as ``standard_attention`` in the lab on "Explain tiled attention and
     verify its output" (section "Read lab.py"), with rows limited to their visible keys. With
     ``subtract_max=False`` the exponentials are taken of the raw scores, which overflows
     (``OverflowError``) for large logits, the failure that page's tests provoke.
+    ``window`` keeps only keys p - W < j <= p of a row at position p.
     Returns (O as a list of rows, LSE as a list).
     """
+    _check_window(causal, window)
     Tq, Tk = len(q), len(k)
     d = len(q[0])
     sc = _default_scale(d, scale)
     out, lse = [], []
     for i in range(Tq):
         last = i + (Tk - Tq) if causal else Tk - 1
+        first = last - int(window) + 1 if window is not None else 0
         scores = []
         for j in range(Tk):
-            if j > last:
+            if j > last or j < first:
                 continue
             acc = 0.0
             for c in range(d):
@@ -137,7 +163,8 @@ def brute_attention(q, k, v, causal: bool, scale: Optional[float] = None,
 # --------------------------------------------------------------------------------------------
 
 def tiled_head(q, k, v, causal: bool, scale: Optional[float] = None, block_q: int = 32,
-               block_kv: int = 32, rescale: bool = True, stats: Optional[dict] = None):
+               block_kv: int = 32, rescale: bool = True, stats: Optional[dict] = None,
+               window: Optional[int] = None):
     """Tiled forward of one head: query blocks outside, key/value blocks inside, online softmax.
 
     Steps in the order of the forward pass on "4.2 FlashAttention I" (section "FlashAttention
@@ -152,7 +179,11 @@ def tiled_head(q, k, v, causal: bool, scale: Optional[float] = None, block_q: in
     ``rescale=False`` drops the rescale of the accumulator (not of l), the planted fault of the
     lab on "Explain tiled attention and verify its output". ``stats`` (a dict) receives the
     number of (query block, key block) tiles visited.
+    With ``window`` the key loop also skips the blocks that end before the window of the block's
+    first query starts, and the tile mask adds the window's left edge: the two-sided skip of
+    exercise 4 of "4.2 FlashAttention I".
     """
+    _check_window(causal, window)
     q, k, v = _f64(q), _f64(k), _f64(v)
     Tq, d = q.shape
     Tk = k.shape[0]
@@ -168,13 +199,21 @@ def tiled_head(q, k, v, causal: bool, scale: Optional[float] = None, block_q: in
         l = np.zeros(i1 - i0)
         acc = np.zeros((i1 - i0, d))
         kv_end = min(Tk, i1 + off) if causal else Tk
+        # first key any row of the block may see: the window's left edge of the first row
+        kv_beg = max(0, i0 + off - int(window) + 1) if window is not None else 0
         for j0 in range(0, kv_end, block_kv):
             j1 = min(j0 + block_kv, Tk)
+            if j1 <= kv_beg:
+                continue
             visited += 1
             S = sc * (qi @ k[j0:j1].T)
             if causal:
                 pos = np.arange(i0, i1)[:, None] + off
-                S = np.where(np.arange(j0, j1)[None, :] > pos, -np.inf, S)
+                cols = np.arange(j0, j1)[None, :]
+                hide = cols > pos
+                if window is not None:
+                    hide = hide | (cols <= pos - int(window))
+                S = np.where(hide, -np.inf, S)
             m_new = np.maximum(m, S.max(axis=1))
             base = np.where(np.isneginf(m_new), 0.0, m_new)
             alpha = np.where(np.isneginf(m), 0.0, np.exp(m - base))
@@ -191,7 +230,8 @@ def tiled_head(q, k, v, causal: bool, scale: Optional[float] = None, block_q: in
 
 
 def tiled_attention(Q, K, V, causal: bool, scale: Optional[float] = None, block_q: int = 32,
-                    block_kv: int = 32, rescale: bool = True, stats: Optional[dict] = None):
+                    block_kv: int = 32, rescale: bool = True, stats: Optional[dict] = None,
+                    window: Optional[int] = None):
     """``tiled_head`` over a whole [B, Hq, Tq, d] problem with grouped kv heads."""
     Q, K, V = np.asarray(Q), np.asarray(K), np.asarray(V)
     B, Hq, Tq, d = Q.shape
@@ -202,7 +242,7 @@ def tiled_attention(Q, K, V, causal: bool, scale: Optional[float] = None, block_
         for h in range(Hq):
             g = _kv_head(h, Hq, Hkv)
             O[b, h], L[b, h] = tiled_head(Q[b, h], K[b, g], V[b, g], causal, scale,
-                                          block_q, block_kv, rescale, stats)
+                                          block_q, block_kv, rescale, stats, window)
     return O, L
 
 
