@@ -101,6 +101,28 @@ int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O, float* LS
 int attn_fwd_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dtype,
                   const fattn_cfg_t* cfg, fattn_cfg_t* out);
 
+/*
+ * attn_fwd_window: sliding-window causal attention ("4.2 FlashAttention I: IO-Awareness & The
+ * Online Softmax", Exercises, exercise 4: a query sees only keys inside a causal window of width
+ * W; "Efficient attention & KV cache", section 7, exercises 1 and 2: the rolling window and the
+ * key loop that starts at the window's left edge). With the bottom-right alignment of attn_fwd,
+ * query row i sits at position p = i + Tk - Tq and sees keys j with p - window < j <= p; key
+ * blocks wholly outside every row's window of a query block are never read.
+ *
+ * Arguments, layouts, ownership, stream semantics and error codes are those of attn_fwd with
+ * causal = 1, plus `window` (keys per row, >= 1; FATTN_ERR_INVALID otherwise). A window of Tk or
+ * more hides nothing beyond the causal mask and gives exactly the result of attn_fwd with
+ * causal = 1. With Tq == 1 and bf16 the split-K decode path reads only the last `window` keys.
+ */
+int attn_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                    int Hq, int Hkv, int Tq, int Tk, int d, int window, float scale, int dtype,
+                    void* stream);
+
+/* attn_fwd_window with an explicit launch configuration, as attn_fwd_cfg is to attn_fwd. */
+int attn_fwd_window_cfg(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                        int Hq, int Hkv, int Tq, int Tk, int d, int window, float scale,
+                        int dtype, void* stream, const fattn_cfg_t* cfg);
+
 /* Text for a return code (static storage). */
 const char* fattn_strerror(int code);
 

@@ -70,6 +70,10 @@ lib.attn_fwd.argtypes = _FWD_ARGS
 lib.attn_fwd.restype = _i
 lib.attn_fwd_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
 lib.attn_fwd_cfg.restype = _i
+lib.attn_fwd_window.argtypes = _FWD_ARGS
+lib.attn_fwd_window.restype = _i
+lib.attn_fwd_window_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
+lib.attn_fwd_window_cfg.restype = _i
 lib.attn_fwd_plan.argtypes = [_i] * 8 + [ctypes.POINTER(FattnCfg), ctypes.POINTER(FattnCfg)]
 lib.attn_fwd_plan.restype = _i
 lib.fattn_strerror.argtypes = [_i]
@@ -132,9 +136,18 @@ def attn_fwd_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg=None) -> dict:
 
 
 def attn_fwd_raw(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream,
-                 cfg=None) -> int:
-    """The C call with plain integers for pointers; returns the library's status code."""
+                 cfg=None, window=None) -> int:
+    """The C call with plain integers for pointers; returns the library's status code.
+
+    With ``window`` set, calls attn_fwd_window[_cfg] (causal implied; ``causal`` is ignored).
+    """
     c = _make_cfg(cfg)
+    if window is not None:
+        if c is None:
+            return lib.attn_fwd_window(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, int(window), scale,
+                                       dtype, stream)
+        return lib.attn_fwd_window_cfg(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, int(window),
+                                       scale, dtype, stream, ctypes.byref(c))
     if c is None:
         return lib.attn_fwd(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream)
     return lib.attn_fwd_cfg(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream,
@@ -142,14 +155,19 @@ def attn_fwd_raw(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, s
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=None, lse=None,
-             cfg=None, stream=None) -> Tuple["object", "object"]:
+             cfg=None, stream=None, window: Optional[int] = None) -> Tuple["object", "object"]:
     """Fused attention forward on torch GPU tensors; returns (o, lse).
 
     q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]; contiguous, all float32 or all bfloat16, on the
     current device. o has q's dtype, lse is float32 [B, Hq, Tq] (natural log). scale defaults to
     1/sqrt(d). The call is enqueued on `stream` (default: torch's current stream).
+    ``window`` (requires ``causal``): sliding-window attention, row at position p sees keys
+    p - window < j <= p (attn_fwd_window).
     """
     import torch
+
+    if window is not None and not causal:
+        raise ValueError("a sliding window is a causal mask: pass causal=True")
 
     if q.dtype == torch.bfloat16:
         dtype = FATTN_BF16
@@ -182,7 +200,8 @@ def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=N
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     rc = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                      B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale), dtype, stream, cfg)
+                      B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), float(scale), dtype, stream, cfg,
+                      window)
     if rc != FATTN_OK:
         raise FattnError(rc, fattn_last_error())
     return out, lse

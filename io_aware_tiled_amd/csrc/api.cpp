@@ -180,10 +180,14 @@ extern "C" int attn_fwd_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int 
   return rc == FATTN_OK ? rc : fail(rc, "launch configuration not implemented for this shape");
 }
 
-extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                            int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
-                            int dtype, void* stream, const fattn_cfg_t* cfg) {
-  g_last_error[0] = 0;
+namespace fattn {
+namespace {
+
+// The forward pass behind every entry point. window == 0: no window; window >= 1: sliding
+// window, causal implied (checked by the callers).
+int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
+            int Hkv, int Tq, int Tk, int d, int causal, int window, float scale, int dtype,
+            void* stream, const fattn_cfg_t* cfg) {
   bool noop;
   int rc = validate_shape(B, Hq, Hkv, Tq, Tk, d, causal, dtype, &noop);
   if (rc != FATTN_OK) return rc;
@@ -192,8 +196,13 @@ extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O
   if (!Q || !K || !V || !O || !LSE) return fail(FATTN_ERR_INVALID, "NULL tensor pointer");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
     return fail(FATTN_ERR_INVALID, "tensor pointer not 16-byte aligned");
+  // A window at least Tk wide hides nothing the causal mask does not: every row's position is
+  // below Tk. Such calls run the plain causal path.
+  if (window >= Tk) window = 0;
+  // Under a window a decode row reads only the last `window` keys: plan the splits on those.
+  const int k0 = (window > 0 && Tq == 1) ? Tk - window : 0;
   fattn_cfg_t plan;
-  rc = make_plan(B, Hq, Hkv, Tq, Tk, d, causal, dtype, cfg, &plan);
+  rc = make_plan(B, Hq, Hkv, Tq, Tk - k0, d, causal, dtype, cfg, &plan);
   if (rc != FATTN_OK) return fail(rc, "launch configuration not implemented for this shape");
 
   Problem p;
@@ -209,6 +218,7 @@ extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O
   p.Tk = Tk;
   p.d = d;
   p.causal = causal;
+  p.window = window;
   p.qsign = scale > 0.f ? 1 : (scale < 0.f ? -1 : 0);
   p.abs_scale = scale == 0.f ? 1.f : std::fabs(scale);
   p.log2_scale = p.abs_scale * kLog2e;
@@ -226,7 +236,8 @@ extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O
       int dev = 0;
       hipError_t he = hipGetDevice(&dev);
       if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipGetDevice", he);
-      const int chunk = ((Tk + plan.splits - 1) / plan.splits + 31) / 32 * 32;
+      const int nkeys = Tk - k0;
+      const int chunk = ((nkeys + plan.splits - 1) / plan.splits + 31) / 32 * 32;
       const size_t rows = (size_t)B * Hq * plan.splits;
       const size_t need = rows * (size_t)d + rows;
       std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -248,7 +259,7 @@ extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O
         ws.ptr = static_cast<float*>(mem);
         ws.floats = need;
       }
-      e = launch_decode_bf16(p, plan.splits, chunk, ws.ptr, ws.ptr + rows * (size_t)d, s);
+      e = launch_decode_bf16(p, k0, plan.splits, chunk, ws.ptr, ws.ptr + rows * (size_t)d, s);
       break;
     }
     default:
@@ -257,11 +268,37 @@ extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O
   return e == hipSuccess ? FATTN_OK : hip_fail(FATTN_ERR_HIP, "kernel launch", e);
 }
 
+}  // namespace
+}  // namespace fattn
+
+extern "C" int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                            int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+                            int dtype, void* stream, const fattn_cfg_t* cfg) {
+  g_last_error[0] = 0;
+  return forward(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, 0, scale, dtype, stream, cfg);
+}
+
 extern "C" int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                         int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale, int dtype,
                         void* stream) {
   return attn_fwd_cfg(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream,
                       nullptr);
+}
+
+extern "C" int attn_fwd_window_cfg(const void* Q, const void* K, const void* V, void* O,
+                                   float* LSE, int B, int Hq, int Hkv, int Tq, int Tk, int d,
+                                   int window, float scale, int dtype, void* stream,
+                                   const fattn_cfg_t* cfg) {
+  g_last_error[0] = 0;
+  if (window < 1) return fail(FATTN_ERR_INVALID, "window must be >= 1");
+  return forward(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, 1, window, scale, dtype, stream, cfg);
+}
+
+extern "C" int attn_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               int B, int Hq, int Hkv, int Tq, int Tk, int d, int window,
+                               float scale, int dtype, void* stream) {
+  return attn_fwd_window_cfg(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, window, scale, dtype,
+                             stream, nullptr);
 }
 
 extern "C" const char* fattn_strerror(int code) {

@@ -78,8 +78,8 @@ __device__ __forceinline__ void load_block(Block<D>& blk, const __bf16* Kh, cons
 template <int D>
 __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hq, int Hkv, int Tk, int splits,
-    int chunk, float log2_scale, int qsign) {
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hq, int Hkv, int Tk, int k0,
+    int splits, int chunk, float log2_scale, int qsign) {
   __shared__ __align__(16) __bf16 Vt[D * VS];
 
   const int lane = threadIdx.x;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
   w /= nqg;
   const int hk = w % Hkv;
   const int b = w / Hkv;
-  const int kbeg = s * chunk;
+  const int kbeg = k0 + s * chunk;  // k0 > 0: a sliding window starts at key Tk - window
   const int kend = min(Tk, kbeg + chunk);
   const int qi = qg * 16 + c16;
   const bool qvalid = qi < G;
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
 }
 
 template <int D>
-hipError_t launch_t(const Problem& p, int splits, int chunk, float* ws_o, float* ws_lse,
+hipError_t launch_t(const Problem& p, int k0, int splits, int chunk, float* ws_o, float* ws_lse,
                     hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   const int nqg = (G + 15) / 16;
@@ -235,8 +235,8 @@ hipError_t launch_t(const Problem& p, int splits, int chunk, float* ws_o, float*
     return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(decode_partial_kernel<D>, dim3((unsigned)grid), dim3(64), 0, stream,
                      static_cast<const __bf16*>(p.Q), static_cast<const __bf16*>(p.K),
-                     static_cast<const __bf16*>(p.V), ws_o, ws_lse, p.Hq, p.Hkv, p.Tk, splits,
-                     chunk, p.log2_scale, p.qsign);
+                     static_cast<const __bf16*>(p.V), ws_o, ws_lse, p.Hq, p.Hkv, p.Tk, k0,
+                     splits, chunk, p.log2_scale, p.qsign);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(D), 0, stream,
@@ -246,12 +246,12 @@ hipError_t launch_t(const Problem& p, int splits, int chunk, float* ws_o, float*
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const Problem& p, int splits, int chunk, float* ws_o,
+hipError_t launch_decode_bf16(const Problem& p, int k0, int splits, int chunk, float* ws_o,
                               float* ws_lse, hipStream_t stream) {
   switch (p.d) {
-    case 32: return launch_t<32>(p, splits, chunk, ws_o, ws_lse, stream);
-    case 64: return launch_t<64>(p, splits, chunk, ws_o, ws_lse, stream);
-    case 128: return launch_t<128>(p, splits, chunk, ws_o, ws_lse, stream);
+    case 32: return launch_t<32>(p, k0, splits, chunk, ws_o, ws_lse, stream);
+    case 64: return launch_t<64>(p, k0, splits, chunk, ws_o, ws_lse, stream);
+    case 128: return launch_t<128>(p, k0, splits, chunk, ws_o, ws_lse, stream);
     default: return hipErrorInvalidValue;
   }
 }

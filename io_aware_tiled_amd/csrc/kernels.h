@@ -18,6 +18,8 @@ struct Problem {
   float* LSE;
   int B, Hq, Hkv, Tq, Tk, d;
   int causal;
+  int window;        // sliding window width (causal only): row at p sees keys p-window < j <= p;
+                     // 0 = no window
   float abs_scale;   // |scale|, or 1 when scale == 0
   float log2_scale;  // abs_scale * log2(e)
   int qsign;
@@ -33,8 +35,9 @@ hipError_t launch_prefill_f32(const Problem& p, hipStream_t stream);
 
 // bf16 split-K decode (Tq == 1): partial kernel + combine kernel on the same stream.
 // ws_o holds splits * B * Hq * d floats, ws_lse splits * B * Hq floats.
-// chunk is the number of keys per split (a multiple of 32); splits = ceil(Tk / chunk).
-hipError_t launch_decode_bf16(const Problem& p, int splits, int chunk, float* ws_o,
+// The keys [k0, Tk) are split into chunks of `chunk` keys (a multiple of 32);
+// splits = ceil((Tk - k0) / chunk). k0 > 0 under a sliding window.
+hipError_t launch_decode_bf16(const Problem& p, int k0, int splits, int chunk, float* ws_o,
                               float* ws_lse, hipStream_t stream);
 
 }  // namespace fattn

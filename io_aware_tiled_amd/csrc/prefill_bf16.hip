@@ -127,7 +127,7 @@ template <int D, int BC, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Tq, int Tk,
-    int causal, float log2_scale, int qsign, int schedule) {
+    int causal, int window, float log2_scale, int qsign, int schedule) {
   using S = Shape<D, BC, NW>;
   // One array per stage, so the compiler can tell a direct-to-LDS load into one stage from reads
   // of another and does not make those reads wait for the load.
@@ -167,10 +167,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   const int q_end = min(i0 + S::BR, Tq);
   const int kv_end = causal ? min(Tk, q_end + off) : Tk;
   const int ntiles = (kv_end + BC - 1) / BC;
-  // tiles [0, jm) need no mask for any row of the workgroup
+  // tiles [0, jm) hold no key past any row's diagonal or past Tk
   int jm = Tk / BC;
   if (causal) jm = min(jm, (i0 + off + 1) / BC);
   jm = min(jm, ntiles);
+  // Sliding window: the first row's window starts at key kv_beg, so the loop starts at tile
+  // j_lo; tiles from j_ul on start at or after the last row's window edge, so no row hides any
+  // of their keys on the left. Tiles in [j_ul, jm) need no mask at all.
+  const int kv_beg = window > 0 ? max(0, i0 + off - window + 1) : 0;
+  const int j_lo = kv_beg / BC;
+  const int j_ul = window > 0 ? (max(0, q_end - 1 + off - window + 1) + BC - 1) / BC : 0;
+  auto clean = [&](int j) { return j >= j_ul && j < jm; };
 
   // ---- this wave's query rows; Q^T operand held in registers for the whole loop
   const int qw0 = i0 + 32 * wave;
@@ -227,12 +234,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
 
   auto mask_tile = [&](f32x16 (&s)[BC / 32], int j0) {
     const int last = causal ? min(Tk - 1, qrow + off) : Tk - 1;
+    const int first = window > 0 ? qrow + off - window + 1 : 0;
 #pragma unroll
     for (int t = 0; t < BC / 32; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = j0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (key > last) s[t][r] = kNegInf;
+        if (key > last || key < first) s[t][r] = kNegInf;
       }
   };
 
@@ -257,7 +265,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     const bool grow = mt > M + kRebase;  // always true on the first tile a row sees
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mt : M;
-      const float alpha = __builtin_amdgcn_exp2f(M - m_new);  // 0 while M is -inf
+      // 0 when M leaves -inf; 1 for a row that still has seen no key (under a sliding window a
+      // row's first tiles can be fully masked while other rows of the wave move their base)
+      const float alpha = m_new == kNegInf ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= alpha;
@@ -300,30 +310,36 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
       }
   };
 
-  auto active = [&](int j) { return wave_has_rows && (!causal || j * BC <= wave_last + off); };
+  // this wave's rows see a key of tile j: not past the diagonal of its last row, not before the
+  // window of its first row
+  auto active = [&](int j) {
+    return wave_has_rows && (!causal || j * BC <= wave_last + off) &&
+           (window == 0 || (j + 1) * BC - 1 >= qw0 + off - window + 1);
+  };
 
   // ---- prologue: clear the V stages (rows past Tk must never hold non-finite leftovers), then
-  // load K(0), V(0), K(1); scores, mask and maximum of tile 0
+  // load K(j_lo), V(j_lo), K(j_lo+1); scores, mask and maximum of tile j_lo. Stages alternate
+  // with j - j_lo.
   for (int i = tid; i < S::TILE / 16; i += S::NT) {
     *(LDS_AS u32x4*)(v_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
     *(LDS_AS u32x4*)(v_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
-  issue_tile(Kh, 0, k_st0);
-  issue_tile(Vh, 0, v_st0);
-  issue_tile(Kh, BC, k_st1);
+  issue_tile(Kh, j_lo * BC, k_st0);
+  issue_tile(Vh, j_lo * BC, v_st0);
+  issue_tile(Kh, (j_lo + 1) * BC, k_st1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sa[BC / 32], sb[BC / 32];
-  if (active(0)) {
+  if (active(j_lo)) {
     qk(sa, k_st0);
-    if (jm == 0) mask_tile(sa, 0);
+    if (!clean(j_lo)) mask_tile(sa, j_lo * BC);
     rebase(sa);
   }
   __syncthreads();
 
-  // ---- steady state: tiles j and j+1 both unmasked and every wave active. Unrolled by two so
-  // the score buffers and LDS stages alternate without copies.
+  // ---- steady state: tiles j, j+1 and j+2 need no mask (so every wave is active). Unrolled by
+  // two so the score buffers and LDS stages alternate without copies.
   auto fast_step = [&](f32x16 (&sc)[BC / 32], f32x16 (&sn)[BC / 32], int j, unsigned char* k_cur,
                        unsigned char* k_nxt, unsigned char* v_cur, unsigned char* v_nxt) {
     const int j0 = j * BC;
@@ -337,25 +353,20 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
-  int j = 0;
-  for (; j + 2 < jm; j += 2) {
-    fast_step(sa, sb, j, k_st0, k_st1, v_st0, v_st1);
-    fast_step(sb, sa, j + 1, k_st1, k_st0, v_st1, v_st0);
-  }
-
-  // ---- remaining tiles: masks, inactive waves and the end of the pipeline
-  for (; j < ntiles; ++j) {
+  // ---- general step: masks, inactive waves, the window's left band and the end of the pipeline
+  auto general_step = [&](int j) {
     const int j0 = j * BC;
-    unsigned char* k_cur = (j & 1) ? k_st1 : k_st0;
-    unsigned char* k_nxt = (j & 1) ? k_st0 : k_st1;
-    unsigned char* v_cur = (j & 1) ? v_st1 : v_st0;
-    unsigned char* v_nxt = (j & 1) ? v_st0 : v_st1;
+    const bool odd = ((j - j_lo) & 1) != 0;
+    unsigned char* k_cur = odd ? k_st1 : k_st0;
+    unsigned char* k_nxt = odd ? k_st0 : k_st1;
+    unsigned char* v_cur = odd ? v_st1 : v_st0;
+    unsigned char* v_nxt = odd ? v_st0 : v_st1;
     issue_tile(Vh, j0 + BC, v_nxt);
     issue_tile(Kh, j0 + 2 * BC, k_cur);
     const bool act_next = (j + 1 < ntiles) && active(j + 1);
     if (act_next) {
       qk(sb, k_nxt);
-      if (j + 1 >= jm) mask_tile(sb, j0 + BC);
+      if (!clean(j + 1)) mask_tile(sb, j0 + BC);
     }
     if (active(j)) {
       bf16x8 pb[BC / 16];
@@ -367,7 +378,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < BC / 32; ++t) sa[t] = sb[t];
+  };
+  // left band of a window (and one step to reach an even stage parity), then the steady state
+  // over clean tiles, then the rest
+  int j = j_lo;
+  for (; j < ntiles && (j < j_ul || ((j - j_lo) & 1) != 0); ++j) general_step(j);
+  for (; j + 2 < jm; j += 2) {
+    fast_step(sa, sb, j, k_st0, k_st1, v_st0, v_st1);
+    fast_step(sb, sa, j + 1, k_st1, k_st0, v_st1, v_st0);
   }
+  for (; j < ntiles; ++j) general_step(j);
 
   // ---- epilogue: O = acc / l, LSE = ln 2 * (M + log2 l)
   if (!wave_has_rows) return;
@@ -402,7 +422,7 @@ hipError_t launch_t(const Problem& p, int schedule, hipStream_t stream) {
                      stream, static_cast<const __bf16*>(p.Q),
                      static_cast<const __bf16*>(p.K), static_cast<const __bf16*>(p.V),
                      static_cast<__bf16*>(p.O), p.LSE, p.B, p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
-                     p.log2_scale, p.qsign, schedule);
+                     p.window, p.log2_scale, p.qsign, schedule);
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@
 // IO-Awareness & The Online Softmax", section "FlashAttention forward: tiling + online softmax
 // fused into one pass"): 32-key tiles of K and V are staged in LDS and read by every lane as
 // broadcasts, each lane keeps its row's running max, running sum and d accumulators in
-// registers, and causal blocks past the diagonal are not visited. Everything is fp32 with the
+// registers, and causal blocks past the diagonal are not visited (nor, under a sliding window,
+// blocks before the window of the block's first row). Everything is fp32 with the
 // accurate exp/log, because this path is held to a 1e-5 absolute bound; the dense fp32 MFMA
 // rate on gfx950 equals the VALU rate, so matrix cores would not make it faster.
 #include <hip/hip_runtime.h>
@@ -23,7 +24,7 @@ template <int D>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Tq, int Tk,
-    int causal, float abs_scale, int qsign) {
+    int causal, int window, float abs_scale, int qsign) {
   __shared__ float4 Ks[BC * D / 4];
   __shared__ float4 Vs[BC * D / 4];
 
@@ -40,9 +41,12 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
   const int i0 = qb * BR;
   const int q_end = min(i0 + BR, Tq);
   const int kv_end = causal ? min(Tk, q_end + off) : Tk;
+  // sliding window: the block starts at the tile holding its first row's first visible key
+  const int kv_beg = window > 0 ? max(0, i0 + off - window + 1) / BC * BC : 0;
   const int row = i0 + lane;
   const bool valid = row < Tq;
   const int last = causal ? min(Tk - 1, row + off) : Tk - 1;
+  const int first = window > 0 ? row + off - window + 1 : 0;
 
   float q[D];
   {
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
   for (int c = 0; c < D; ++c) acc[c] = 0.f;
   float m = kNegInf, l = 0.f;
 
-  for (int j0 = 0; j0 < kv_end; j0 += BC) {
+  for (int j0 = kv_beg; j0 < kv_end; j0 += BC) {
     for (int i = lane; i < BC * D / 4; i += 64) {
       const int key = j0 + i / (D / 4);
       const int c4 = i % (D / 4);
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
         dot = fmaf(q[4 * c + 2], kx.z, dot);
         dot = fmaf(q[4 * c + 3], kx.w, dot);
       }
-      s[jj] = (j0 + jj <= last) ? dot * abs_scale : kNegInf;
+      s[jj] = (j0 + jj <= last && j0 + jj >= first) ? dot * abs_scale : kNegInf;
       mt = fmaxf(mt, s[jj]);
     }
     const float m_new = fmaxf(m, mt);
@@ -137,7 +141,7 @@ hipError_t launch_t(const Problem& p, hipStream_t stream) {
   hipLaunchKernelGGL(prefill_f32_kernel<D>, dim3((unsigned)grid), dim3(64), 0, stream,
                      static_cast<const float*>(p.Q), static_cast<const float*>(p.K),
                      static_cast<const float*>(p.V), static_cast<float*>(p.O), p.LSE, p.B, p.Hq,
-                     p.Hkv, p.Tq, p.Tk, p.causal, p.abs_scale, p.qsign);
+                     p.Hkv, p.Tq, p.Tk, p.causal, p.window, p.abs_scale, p.qsign);
   return hipGetLastError();
 }
 

@@ -50,7 +50,30 @@ def _call(**kw):
     a.update(kw)
     return fa.attn_fwd_raw(a["Q"], a["K"], a["V"], a["O"], a["LSE"], a["B"], a["Hq"], a["Hkv"],
                            a["Tq"], a["Tk"], a["d"], a["causal"], a["scale"], a["dtype"],
-                           a["stream"], kw.get("cfg"))
+                           a["stream"], kw.get("cfg"), kw.get("window"))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(window=0), dict(window=-5), dict(window=8, Q=None), dict(window=8, Tq=65, Tk=64),
+    dict(window=8, Hkv=3), dict(window=8, O=P + 2), dict(window=0, cfg=dict(block_kv=64)),
+])
+def test_window_invalid_arguments(kw):
+    assert _call(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(window=16, B=0), dict(window=1, Tq=0),
+                                dict(window=3, B=0, Q=None, K=None, V=None, O=None, LSE=None)])
+def test_window_empty_problems_are_noops(kw):
+    assert _call(**kw) == OK
+
+
+def test_window_unsupported_head_dim():
+    assert _call(window=16, d=96) == UNSUPPORTED
+
+
+def test_python_binding_rejects_a_noncausal_window():
+    with pytest.raises(ValueError):
+        fa.attn_fwd(None, None, None, causal=False, window=4)
 
 
 @pytest.mark.parametrize("kw", [
