@@ -7,9 +7,14 @@ One step is one pass of the whole hot path on synthetic, seeded inputs already r
   * GQA decode, bf16, B=64, Hq=64, Hkv=8, Tq=1, Tk=8192, d=128 (one attn_fwd call: split-K
     partial kernel + combine kernel).
 Each call is bracketed by HIP events recorded on the stream the kernels are launched on. The
-headline value is the prefill rate in TFLOP/s, counting 4*B*H*T^2*d halved for the causal mask;
-the decode rate is reported as algorithmic HBM bytes per second (K and V read once, Q read,
-O and LSE written). One JSON line is printed.
+headline value is the prefill rate in TFLOP/s from the median call time, counting 4*B*H*T^2*d
+halved for the causal mask; the decode rate is reported as algorithmic HBM bytes per second
+(K and V read once, Q read, O and LSE written). Mean, p10 and p90 call times are reported too.
+
+After the timed steps, and outside them: the library's two probes (matrix-core rate on
+register operands, nontemporal HBM read rate) give the achievable rates the two kernels are also
+quoted against, and the sliding-window variants of both calls (window 4096) are timed, with the
+work of the visible (query, key) pairs only. One JSON line is printed.
 
     python bench.py --calibrate-copy BYTES
 
@@ -48,6 +53,70 @@ def prefill_flops(B, H, Tq, Tk, d, causal):
 def decode_bytes(B, Hq, Hkv, Tk, d, eb=2):
     """K and V read once, Q read, O written (element size eb), LSE written in fp32."""
     return (2 * B * Hkv * Tk * d + 2 * B * Hq * d) * eb + 4 * B * Hq
+
+
+def window_pairs(T, W):
+    """Visible (query, key) pairs of a square causal window: row i sees min(i + 1, W) keys."""
+    if W >= T:
+        return T * (T + 1) // 2
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def window_decode_bytes(B, Hq, Hkv, W, d, eb=2):
+    """A decode step under a window reads only the last W keys and values."""
+    return decode_bytes(B, Hq, Hkv, W, d, eb)
+
+
+def stats_ms(times):
+    """median, mean, p10, p90 of a list of call times in ms."""
+    import numpy as np
+
+    a = np.asarray(times, dtype=np.float64)
+    return {"median": float(np.median(a)), "mean": float(a.mean()),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90))}
+
+
+def time_calls(torch, fn, warmup, reps):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        fn()
+        e[1].record()
+    torch.cuda.synchronize()
+    return [e[0].elapsed_time(e[1]) for e in ev]
+
+
+def probes(fa, torch):
+    """Matrix-core TFLOP/s and HBM read GB/s of the library's probes (best of a few launches)."""
+    wgs, iters = 2048, 100
+    out = torch.empty(wgs * 512, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def mfma():
+        rc = fa.lib.fattn_probe_mfma(out.data_ptr(), wgs, iters, stream)
+        assert rc == fa.FATTN_OK, rc
+
+    t = time_calls(torch, mfma, 3, 5)
+    mfma_tflops = wgs * 8 * 32 * iters * 32768.0 / (min(t) * 1e-3) / 1e12
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    rwgs = 8192
+    words = torch.empty(rwgs * 256, dtype=torch.int32, device="cuda")
+
+    def read():
+        rc = fa.lib.fattn_probe_hbm_read(buf.data_ptr(), nbytes, words.data_ptr(), rwgs, stream)
+        assert rc == fa.FATTN_OK, rc
+
+    t = time_calls(torch, read, 3, 5)
+    read_gbs = nbytes / (min(t) * 1e-3) / 1e9
+    del buf, words, out
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "hbm_read_gbs": round(read_gbs, 1),
+            "what": "best of 5 launches: 4 chains of v_mfma_f32_32x32x16_bf16 per wavefront on "
+                    "register operands (2048 x 8 wavefronts); 16-byte nontemporal loads over a "
+                    "4 GiB buffer (8192 x 256 threads)"}
 
 
 def source_hash(name):
@@ -117,6 +186,10 @@ def cpu_baseline(budget_s=12.0, max_heads=32):
                       f"each, fp64 dense (S and P materialised), {elapsed:.2f} s; TFLOP/s with "
                       f"the same causal-halved FLOP count as the GPU figure",
             "seconds": elapsed, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def _r(d):
+    return {k: round(v, 4) for k, v in d.items()}
 
 
 def calibrate_copy(nbytes, reps=3):
@@ -192,8 +265,9 @@ def main():
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prefill_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    decode_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    pst = stats_ms([e[0].elapsed_time(e[1]) for e in ev])
+    dst = stats_ms([e[1].elapsed_time(e[2]) for e in ev])
+    prefill_ms, decode_ms = pst["median"], dst["median"]
     if not (bool(torch.isfinite(o3).all()) and bool(torch.isfinite(o4).all())):
         print("non-finite output", file=sys.stderr)
         sys.exit(1)
@@ -202,6 +276,19 @@ def main():
     tflops = flops / (prefill_ms * 1e-3) / 1e12
     dbytes = decode_bytes(dc.B, dc.Hq, dc.Hkv, dc.Tk, dc.d)
     gbs = dbytes / (decode_ms * 1e-3) / 1e9
+
+    # ---- outside the timed steps: achievable rates, then the sliding-window variants
+    print("[bench] probes and sliding-window calls", file=sys.stderr, flush=True)
+    pr = probes(fa, torch)
+    W = 4096
+    sw_p = stats_ms(time_calls(torch, lambda: fa.attn_fwd(q3, k3, v3, causal=True, scale=pc.scale,
+                                                         out=o3, lse=l3, window=W), 10, 20))
+    sw_d = stats_ms(time_calls(torch, lambda: fa.attn_fwd(q4, k4, v4, causal=True, scale=dc.scale,
+                                                         out=o4, lse=l4, window=W), 10, 20))
+    sw_flops = 4.0 * pc.d * pc.B * pc.Hq * window_pairs(pc.Tq, W)
+    sw_tflops = sw_flops / (sw_p["median"] * 1e-3) / 1e12
+    sw_bytes = window_decode_bytes(dc.B, dc.Hq, dc.Hkv, W, dc.d)
+    sw_gbs = sw_bytes / (sw_d["median"] * 1e-3) / 1e9
 
     cpu = None
     if args.cpu_baseline == "auto":
@@ -230,10 +317,12 @@ def main():
         },
         "prefill": {"ms": round(prefill_ms, 4), "tflops": round(tflops, 2),
                     "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-                    "flops_per_call": flops},
+                    "pct_of_probe": round(100 * tflops / pr["mfma_bf16_tflops"], 2),
+                    "flops_per_call": flops, "ms_stats": _r(pst)},
         "decode": {"ms": round(decode_ms, 4), "gbs": round(gbs, 1),
                    "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-                   "bytes_per_call": dbytes,
+                   "pct_of_probe": round(100 * gbs / pr["hbm_read_gbs"], 2),
+                   "bytes_per_call": dbytes, "ms_stats": _r(dst),
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -241,6 +330,19 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for("prefill_bf16.hip", "prefill")},
+        "probes": pr,
+        "sliding_window": {
+            "window": W,
+            "prefill": {"ms": round(sw_p["median"], 4), "tflops": round(sw_tflops, 2),
+                        "pct_mfma_peak": round(100 * sw_tflops / PEAK_BF16_TFLOPS, 2),
+                        "flops_per_call": sw_flops, "ms_stats": _r(sw_p),
+                        "work": "4*d FLOPs per visible (query, key) pair, window 4096"},
+            "decode": {"ms": round(sw_d["median"], 4), "gbs": round(sw_gbs, 1),
+                       "pct_hbm_peak": round(100 * sw_gbs / PEAK_HBM_GBS, 2),
+                       "bytes_per_call": sw_bytes, "ms_stats": _r(sw_d),
+                       "work": "K and V of the last 4096 keys read once, Q read, O and LSE "
+                               "written"},
+        },
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

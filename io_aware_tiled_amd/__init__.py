@@ -75,6 +75,10 @@ lib.attn_fwd_window.restype = _i
 lib.attn_fwd_window_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
 lib.attn_fwd_window_cfg.restype = _i
 lib.attn_fwd_plan.argtypes = [_i] * 8 + [ctypes.POINTER(FattnCfg), ctypes.POINTER(FattnCfg)]
+lib.fattn_probe_mfma.argtypes = [_vp, _i, _i, _vp]
+lib.fattn_probe_mfma.restype = _i
+lib.fattn_probe_hbm_read.argtypes = [_vp, ctypes.c_size_t, _vp, _i, _vp]
+lib.fattn_probe_hbm_read.restype = _i
 lib.attn_fwd_plan.restype = _i
 lib.fattn_strerror.argtypes = [_i]
 lib.fattn_strerror.restype = ctypes.c_char_p

@@ -1,0 +1,83 @@
+// Measurement probes (not part of the attention path): the matrix-core and HBM-read rates this
+// chip reaches on trivial work, so that the attention kernels' rates can be quoted against what
+// is achievable as well as against the published peaks.
+//
+//  * fattn_probe_mfma: every wavefront runs four independent chains of
+//    v_mfma_f32_32x32x16_bf16 (the prefill kernel's instruction) on register operands, eight
+//    wavefronts per workgroup; 32768 FLOPs per instruction.
+//  * fattn_probe_hbm_read: grid-stride 16-byte nontemporal loads over a buffer (the decode
+//    kernel's load form), one XOR-reduced word stored per thread.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "fattn.h"
+
+namespace fattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(512) void probe_mfma_kernel(float* __restrict__ out, int iters) {
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)(threadIdx.x + i));
+    b[i] = (__bf16)(0.002f * (float)((int)threadIdx.x - i));
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ p, size_t n,
+                                                         unsigned* __restrict__ out) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
+  }
+  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+}  // namespace
+}  // namespace fattn
+
+using namespace fattn;
+
+extern "C" int fattn_probe_mfma(float* out, int workgroups, int iters, void* stream) {
+  if (!out || workgroups <= 0 || iters <= 0) return FATTN_ERR_INVALID;
+  hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)workgroups), dim3(512), 0,
+                     reinterpret_cast<hipStream_t>(stream), out, iters);
+  return hipGetLastError() == hipSuccess ? FATTN_OK : FATTN_ERR_HIP;
+}
+
+extern "C" int fattn_probe_hbm_read(const void* buf, size_t bytes, unsigned* out,
+                                    int workgroups, void* stream) {
+  if (!buf || !out || workgroups <= 0 || bytes < 16 || (bytes & 15) != 0 ||
+      (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+    return FATTN_ERR_INVALID;
+  hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)workgroups), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf),
+                     bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? FATTN_OK : FATTN_ERR_HIP;
+}

@@ -1,0 +1,28 @@
+"""The benchmark's own work formulas agree with the oracle's accounting (CPU only)."""
+
+import pytest
+
+import bench
+from oracle import accounting as acc
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 8192, 8192, 128, True), (4, 16, 1024, 1024, 64, True),
+                                   (1, 32, 4096, 4096, 128, False)])
+def test_prefill_flops(shape):
+    B, H, Tq, Tk, d, causal = shape
+    assert bench.prefill_flops(B, H, Tq, Tk, d, causal) == acc.attention_flops(B, H, Tq, Tk, d,
+                                                                               causal)
+
+
+def test_decode_bytes():
+    assert bench.decode_bytes(64, 64, 8, 8192, 128) == acc.decode_bytes(64, 64, 8, 8192, 128)
+
+
+@pytest.mark.parametrize("T,W", [(10, 3), (5, 10), (257, 64), (1000, 1), (64, 64)])
+def test_window_pairs(T, W):
+    assert bench.window_pairs(T, W) == acc.visible_pairs(T, T, True, W)
+
+
+def test_window_decode_bytes_read_only_the_window():
+    assert bench.window_decode_bytes(64, 64, 8, 4096, 128) == acc.decode_bytes(64, 64, 8, 4096,
+                                                                               128)
