@@ -336,12 +336,14 @@ def main():
             "prefill": {"ms": round(sw_p["median"], 4), "tflops": round(sw_tflops, 2),
                         "pct_mfma_peak": round(100 * sw_tflops / PEAK_BF16_TFLOPS, 2),
                         "flops_per_call": sw_flops, "ms_stats": _r(sw_p),
-                        "work": "4*d FLOPs per visible (query, key) pair, window 4096"},
+                        "work": "4*d FLOPs per visible (query, key) pair, window 4096",
+                        "traffic": traffic_for("prefill_bf16.hip", "prefill_window")},
             "decode": {"ms": round(sw_d["median"], 4), "gbs": round(sw_gbs, 1),
                        "pct_hbm_peak": round(100 * sw_gbs / PEAK_HBM_GBS, 2),
                        "bytes_per_call": sw_bytes, "ms_stats": _r(sw_d),
                        "work": "K and V of the last 4096 keys read once, Q read, O and LSE "
-                               "written"},
+                               "written",
+                       "traffic": traffic_for("decode_bf16.hip", "decode_window")},
         },
         "cpu_baseline": cpu,
     }
