@@ -1,4 +1,4 @@
-"""CPU oracle for the fused attention forward pass.
+"""CPU oracle for the fused attention forward pass and its gradients.
 
 TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline leg
 may import anything from this package; the product path (the HIP library and its Python binding)
@@ -12,9 +12,10 @@ the five pages on tiled/online-softmax attention:
   * "Attention from scratch + roofline" (LLM systems cookbook),
   * "Efficient attention & KV cache" (ML interview book).
 
-Parity status: every function below is pinned by `tests/test_oracle_pins.py` and
-`tests/test_accounting.py` against values the pages print, closed forms, invariants and library
-special cases. No function is "parity unpinned".
+Parity status: every function below is pinned by `tests/test_oracle_pins.py`,
+`tests/test_window_pins.py`, `tests/test_backward_pins.py` and `tests/test_accounting.py` against
+values the pages print, closed forms, invariants, finite differences and library special cases.
+No function is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -27,5 +28,12 @@ from .attention import (  # noqa: F401
     online_softmax_weighted_sum,
     tiled_attention,
     tiled_head,
+)
+from .backward import (  # noqa: F401
+    backward_flops,
+    dense_backward,
+    dense_backward_head,
+    loss_gradient_fd,
+    tiled_backward_head,
 )
 from . import accounting  # noqa: F401

@@ -1,0 +1,107 @@
+"""Pins of the backward oracle (CPU only): finite differences, torch float64 autograd, the
+pages' tiled backward, closed forms and invariants of the gradients."""
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def test_pages_gradient_check():
+    # "4.2 FlashAttention I", section "The backward pass": seed 2, N = 48, d = 8, causal,
+    # 16 x 16 tiles; central differences of sum(dO * O) agree to about 1e-7.
+    rng = np.random.default_rng(2)
+    N, d = 48, 8
+    Q = rng.normal(size=(N, d)); K = rng.normal(size=(N, d)); V = rng.normal(size=(N, d))
+    O, L = oracle.tiled_head(Q, K, V, True, block_q=16, block_kv=16)
+    dO = rng.normal(size=(N, d))
+    dQ, dK, dV = oracle.tiled_backward_head(Q, K, V, O, L, dO, True, block_q=16, block_kv=16)
+    err = max(abs(oracle.loss_gradient_fd(Q, K, V, dO, True, "q", (3, 2)) - dQ[3, 2]),
+              abs(oracle.loss_gradient_fd(Q, K, V, dO, True, "k", (5, 1)) - dK[5, 1]),
+              abs(oracle.loss_gradient_fd(Q, K, V, dO, True, "v", (7, 4)) - dV[7, 4]))
+    assert err < 1e-6
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 5)])
+@pytest.mark.parametrize("Tq,Tk", [(12, 12), (7, 15)])
+def test_dense_backward_against_finite_differences(causal, window, Tq, Tk):
+    if causal and Tq > Tk:
+        pytest.skip("causal needs Tq <= Tk")
+    d = 6
+    q, k, v, do = _rand((Tq, d), 1), _rand((Tk, d), 2), _rand((Tk, d), 3), _rand((Tq, d), 4)
+    dQ, dK, dV, *_ = oracle.dense_backward_head(q, k, v, do, causal, 0.6, window)
+    rng = np.random.default_rng(5)
+    for which, g, shape in (("q", dQ, (Tq, d)), ("k", dK, (Tk, d)), ("v", dV, (Tk, d))):
+        for _ in range(6):
+            idx = (int(rng.integers(shape[0])), int(rng.integers(shape[1])))
+            fd = oracle.loss_gradient_fd(q, k, v, do, causal, which, idx, 0.6, window=window)
+            assert abs(fd - g[idx]) < 1e-7, (which, idx)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_backward_against_torch_autograd_fp64(causal):
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, Tq, Tk, d = 2, 4, 2, 20, 33, 8
+    rng = np.random.default_rng(6)
+    Q = rng.standard_normal((B, Hq, Tq, d)); K = rng.standard_normal((B, Hkv, Tk, d))
+    V = rng.standard_normal((B, Hkv, Tk, d)); dO = rng.standard_normal((B, Hq, Tq, d))
+    dQ, dK, dV = oracle.dense_backward(Q, K, V, dO, causal, 0.35)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    mask = None
+    if causal:  # torch's is_causal is top-left; pass the bottom-right mask explicitly
+        pos = np.arange(Tq)[:, None] + (Tk - Tq)
+        mask = torch.from_numpy(np.arange(Tk)[None, :] <= pos)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.35,
+                                                         enable_gqa=True)
+    o.backward(torch.from_numpy(dO))
+    for mine, t in ((dQ, tq), (dK, tk), (dV, tv)):
+        assert np.max(np.abs(mine - t.grad.numpy())) <= 1e-12
+
+
+@pytest.mark.parametrize("block", [1, 7, 16, 64])
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 9)])
+def test_tiled_backward_equals_dense(block, causal, window):
+    T, d = 70, 8
+    q, k, v, do = _rand((T, d), 7), _rand((T, d), 8), _rand((T, d), 9), _rand((T, d), 10)
+    dQ, dK, dV, O, L, _ = oracle.dense_backward_head(q, k, v, do, causal, None, window)
+    tQ, tK, tV = oracle.tiled_backward_head(q, k, v, O, L, do, causal, None, block, block, window)
+    for a, b in ((dQ, tQ), (dK, tK), (dV, tV)):
+        assert np.max(np.abs(a - b)) <= 1e-12
+
+
+def test_d_is_the_row_sum_of_p_times_dp():
+    Tq, Tk, d = 9, 13, 5
+    q, k, v, do = _rand((Tq, d), 11), _rand((Tk, d), 12), _rand((Tk, d), 13), _rand((Tq, d), 14)
+    _, _, _, _, _, D = oracle.dense_backward_head(q, k, v, do, True)
+    _, _, P = oracle.dense_head(q, k, v, True, return_p=True)
+    assert np.max(np.abs(D - np.sum(P * (do @ v.T), axis=1))) <= 1e-13
+
+
+def test_single_key_closed_forms():
+    # one key: P = 1 whatever the scores, so dQ = dK = 0 and dV = sum of the dO rows
+    q, k, v, do = _rand((5, 4), 15), _rand((1, 4), 16), _rand((1, 4), 17), _rand((5, 4), 18)
+    dQ, dK, dV, *_ = oracle.dense_backward_head(q, k, v, do, False)
+    assert np.max(np.abs(dQ)) <= 1e-15 and np.max(np.abs(dK)) <= 1e-15
+    assert np.max(np.abs(dV[0] - do.sum(axis=0))) <= 1e-14
+    # causal row 0 sees one key: its dQ row is 0
+    q, k, v, do = _rand((6, 4), 19), _rand((6, 4), 20), _rand((6, 4), 21), _rand((6, 4), 22)
+    dQ, *_ = oracle.dense_backward_head(q, k, v, do, True)
+    assert np.max(np.abs(dQ[0])) <= 1e-15
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_gradients_sum_to_zero(causal):
+    # every row of dS sums to 0 (softmax is invariant to adding a constant to a row's scores),
+    # so sum_j dK_j = scale * sum_i q_i * sum_j dS_ij = 0
+    q, k, v, do = _rand((11, 6), 23), _rand((11, 6), 24), _rand((11, 6), 25), _rand((11, 6), 26)
+    _, dK, *_ = oracle.dense_backward_head(q, k, v, do, causal)
+    assert np.max(np.abs(dK.sum(axis=0))) <= 1e-13
+
+
+def test_backward_flops_convention():
+    assert oracle.backward_flops(1, 32, 8192, 8192, 128, True) == 10 * 32 * 8192 ** 2 * 128 / 2
+    assert oracle.backward_flops(2, 4, 100, 50, 64, False) == 10 * 2 * 4 * 100 * 50 * 64
