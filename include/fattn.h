@@ -31,7 +31,7 @@ extern "C" {
 #define FATTN_ERR_INVALID (-1)     /* an argument is out of its documented range */
 #define FATTN_ERR_UNSUPPORTED (-2) /* valid but not implemented (head dim not 32, 64 or 128) */
 #define FATTN_ERR_HIP (-3)         /* the HIP runtime reported an error at launch */
-#define FATTN_ERR_NOMEM (-4)       /* the split-K workspace could not be allocated */
+#define FATTN_ERR_NOMEM (-4)       /* a workspace could not be allocated */
 
 /* Element types of Q, K, V and O. LSE is always float32. */
 #define FATTN_F32 0
@@ -125,6 +125,35 @@ int attn_fwd_window_cfg(const void* Q, const void* K, const void* V, void* O, fl
                         int Hq, int Hkv, int Tq, int Tk, int d, int window, float scale,
                         int dtype, void* stream, const fattn_cfg_t* cfg);
 
+/*
+ * attn_bwd: enqueue the backward pass of attn_fwd (or attn_fwd_window) on `stream`: the
+ * gradients of a scalar loss with respect to Q, K and V, given its gradient dO with respect to
+ * O. The probabilities are recomputed tile by tile from Q, K and the saved LSE instead of being
+ * stored ("4.2 FlashAttention I: IO-Awareness & The Online Softmax", section "The backward pass:
+ * recomputation instead of storage"; "Efficient attention & KV cache", section 2.2):
+ *   P = exp(scale * Q K^T + mask - LSE),  D_i = sum_c dO[i,c] O[i,c],
+ *   dV = P^T dO,  dS = P o (dO V^T - D),  dQ = scale * dS K,  dK = scale * dS^T Q,
+ * with the gradients of kv head g summed over the query heads h / (Hq / Hkv) == g that read it.
+ *
+ *   Q, dO, O, dQ  [B, Hq,  Tq, d] contiguous bf16 (dQ written)
+ *   K, V, dK, dV  [B, Hkv, Tk, d] contiguous bf16 (dK, dV written)
+ *   LSE           [B, Hq,  Tq]    contiguous float32, as written by the forward call
+ * O and LSE must be the forward outputs for the same Q, K, V, causal, window and scale. `window`
+ * is 0 for none, else the sliding-window width of attn_fwd_window (causal must then be 1).
+ * All pointers are caller-owned device pointers on the current device, 16-byte aligned. dQ, dK
+ * and dV must not overlap the inputs. The result is bitwise reproducible: no atomics, fixed
+ * summation order.
+ *
+ * Errors: those of attn_fwd, plus FATTN_ERR_INVALID for a negative window or a window without
+ * causal; dtype FATTN_F32 returns FATTN_ERR_UNSUPPORTED. B == 0, Hq == 0 or Tq == 0 is a no-op.
+ * The call uses a grow-only workspace per (device, stream) of B * Hq * ceil(Tq / 32) * 256 bytes
+ * (FATTN_ERR_NOMEM if it cannot be allocated), shared with the decode path and freed by
+ * fattn_release().
+ */
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, void* dQ, void* dK, void* dV, int B, int Hq, int Hkv, int Tq,
+             int Tk, int d, int causal, int window, float scale, int dtype, void* stream);
+
 /* Text for a return code (static storage). */
 const char* fattn_strerror(int code);
 
@@ -139,7 +168,7 @@ const char* fattn_last_error(void);
 int fattn_version(void);
 
 /*
- * Free the decode workspaces of every device after synchronising each device. Safe to call at
+ * Free the workspaces (decode, backward) of every device after synchronising each device. Safe to call at
  * any time when no call of this library is in flight; later calls allocate again.
  */
 int fattn_release(void);

@@ -1,10 +1,11 @@
-"""Python binding of libfattn, the MI355X fused attention forward library.
+"""Python binding of libfattn, the MI355X fused attention library (forward and backward).
 
 Argument marshalling only: every step of the computation runs in the HIP kernels of
 libfattn.so; torch supplies device memory and the current stream. Importing this package loads
 the in-tree library and fails loudly if it has not been built.
 
     o, lse = attn_fwd(q, k, v, causal=True)      # q [B,Hq,Tq,d], k/v [B,Hkv,Tk,d] on the GPU
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=True)
 """
 
 from __future__ import annotations
@@ -74,6 +75,8 @@ lib.attn_fwd_window.argtypes = _FWD_ARGS
 lib.attn_fwd_window.restype = _i
 lib.attn_fwd_window_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
 lib.attn_fwd_window_cfg.restype = _i
+lib.attn_bwd.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _vp]
+lib.attn_bwd.restype = _i
 lib.attn_fwd_plan.argtypes = [_i] * 8 + [ctypes.POINTER(FattnCfg), ctypes.POINTER(FattnCfg)]
 lib.fattn_probe_mfma.argtypes = [_vp, _i, _i, _vp]
 lib.fattn_probe_mfma.restype = _i
@@ -209,3 +212,57 @@ def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=N
     if rc != FATTN_OK:
         raise FattnError(rc, fattn_last_error())
     return out, lse
+
+
+def attn_bwd_raw(Q, K, V, O, dO, LSE, dQ, dK, dV, B, Hq, Hkv, Tq, Tk, d, causal, window, scale,
+                 dtype, stream) -> int:
+    """The C call attn_bwd with plain integers for pointers; returns the library's status code."""
+    return lib.attn_bwd(Q, K, V, O, dO, LSE, dQ, dK, dV, B, Hq, Hkv, Tq, Tk, d, causal, window,
+                        scale, dtype, stream)
+
+
+def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None,
+             window: Optional[int] = None, dq=None, dk=None, dv=None, stream=None):
+    """Backward of attn_fwd on torch GPU tensors; returns (dq, dk, dv).
+
+    q, o, do: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d]; bfloat16, contiguous, on the current
+    device; lse: float32 [B, Hq, Tq] from the forward call with the same causal, window and
+    scale (default 1/sqrt(d)). Enqueued on `stream` (default: torch's current stream).
+    """
+    import torch
+
+    if window is not None and not causal:
+        raise ValueError("a sliding window is a causal mask: pass causal=True")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk_ = k.shape
+    if (Bk, dk_) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("o and do must have q's shape")
+    if tuple(lse.shape) != (B, Hq, Tq):
+        raise ValueError("lse must be [B, Hq, Tq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Tq,
+                      Tk, d, int(bool(causal)), int(window or 0), float(scale), FATTN_BF16, stream)
+    if rc != FATTN_OK:
+        raise FattnError(rc, fattn_last_error())
+    return dq, dk, dv

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libfattn.so")
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip", "probe.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip", "backward_bf16.hip",
+           "probe.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -160,6 +160,31 @@ struct Workspace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
 
+// The workspace of (dev, stream), grown to at least `need` floats. Call with g_ws_mutex held.
+// Growing waits for the stream (earlier work may still read the old buffer) and frees it.
+int workspace(int dev, hipStream_t s, size_t need, float** out) {
+  Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
+  if (ws.floats < need) {
+    if (ws.ptr) {
+      hipError_t he = hipStreamSynchronize(s);
+      if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipStreamSynchronize", he);
+      (void)hipFree(ws.ptr);
+      ws.ptr = nullptr;
+      ws.floats = 0;
+    }
+    void* mem = nullptr;
+    hipError_t he = hipMalloc(&mem, need * sizeof(float));
+    if (he != hipSuccess) {
+      (void)hipGetLastError();
+      return hip_fail(FATTN_ERR_NOMEM, "hipMalloc of the workspace", he);
+    }
+    ws.ptr = static_cast<float*>(mem);
+    ws.floats = need;
+  }
+  *out = ws.ptr;
+  return FATTN_OK;
+}
+
 }  // namespace
 }  // namespace fattn
 
@@ -241,25 +266,10 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
       const size_t rows = (size_t)B * Hq * plan.splits;
       const size_t need = rows * (size_t)d + rows;
       std::lock_guard<std::mutex> lock(g_ws_mutex);
-      Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(stream)}];
-      if (ws.floats < need) {
-        if (ws.ptr) {
-          he = hipStreamSynchronize(s);
-          if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipStreamSynchronize", he);
-          (void)hipFree(ws.ptr);
-          ws.ptr = nullptr;
-          ws.floats = 0;
-        }
-        void* mem = nullptr;
-        he = hipMalloc(&mem, need * sizeof(float));
-        if (he != hipSuccess) {
-          (void)hipGetLastError();
-          return hip_fail(FATTN_ERR_NOMEM, "hipMalloc of the decode workspace", he);
-        }
-        ws.ptr = static_cast<float*>(mem);
-        ws.floats = need;
-      }
-      e = launch_decode_bf16(p, k0, plan.splits, chunk, ws.ptr, ws.ptr + rows * (size_t)d, s);
+      float* ws = nullptr;
+      rc = workspace(dev, s, need, &ws);
+      if (rc != FATTN_OK) return rc;
+      e = launch_decode_bf16(p, k0, plan.splits, chunk, ws, ws + rows * (size_t)d, s);
       break;
     }
     default:
@@ -301,13 +311,64 @@ extern "C" int attn_fwd_window(const void* Q, const void* K, const void* V, void
                              stream, nullptr);
 }
 
+extern "C" int attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
+                        int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window,
+                        float scale, int dtype, void* stream) {
+  g_last_error[0] = 0;
+  bool noop;
+  int rc = validate_shape(B, Hq, Hkv, Tq, Tk, d, causal, dtype, &noop);
+  if (rc != FATTN_OK) return rc;
+  if (!std::isfinite(scale)) return fail(FATTN_ERR_INVALID, "scale is not finite");
+  if (window < 0) return fail(FATTN_ERR_INVALID, "window must be >= 0");
+  if (window > 0 && !causal) return fail(FATTN_ERR_INVALID, "a window needs causal = 1");
+  if (noop) return FATTN_OK;
+  if (dtype != FATTN_BF16) return fail(FATTN_ERR_UNSUPPORTED, "backward is bf16 only");
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(FATTN_ERR_INVALID, "NULL tensor pointer");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+    return fail(FATTN_ERR_INVALID, "tensor pointer not 16-byte aligned");
+  if (window >= Tk) window = 0;
+
+  BwdProblem p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.dO = dO;
+  p.LSE = LSE;
+  p.dQ = dQ;
+  p.dK = dK;
+  p.dV = dV;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Tq = Tq;
+  p.Tk = Tk;
+  p.d = d;
+  p.causal = causal;
+  p.window = window;
+  p.scale = scale;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipGetDevice", he);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  float* ws = nullptr;
+  rc = workspace(dev, s, backward_workspace_floats(B, Hq, Tq), &ws);
+  if (rc != FATTN_OK) return rc;
+  he = launch_backward_bf16(p, ws, s);
+  return he == hipSuccess ? FATTN_OK : hip_fail(FATTN_ERR_HIP, "kernel launch", he);
+}
+
 extern "C" const char* fattn_strerror(int code) {
   switch (code) {
     case FATTN_OK: return "ok";
     case FATTN_ERR_INVALID: return "invalid argument";
     case FATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case FATTN_ERR_HIP: return "HIP runtime error";
-    case FATTN_ERR_NOMEM: return "out of device memory for the decode workspace";
+    case FATTN_ERR_NOMEM: return "out of device memory for the workspace";
     default: return "unknown error code";
   }
 }

@@ -1,0 +1,525 @@
+// Backward pass of attention with recomputation, bf16 in and out, fp32 accumulation.
+//
+// "4.2 FlashAttention I: IO-Awareness & The Online Softmax" (section "The backward pass:
+// recomputation instead of storage") and "Efficient attention & KV cache" (section 2.2, the
+// backward with recomputation): the forward keeps only O and the per-row log-sum-exp L; the
+// backward rebuilds each probability tile as P = exp(scale * Q K^T - L) instead of reading a
+// stored T x T matrix, and with D_i = rowsum(dO o O)_i:
+//   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+//
+// Three kernels, none with atomics, so every result is bitwise reproducible run to run:
+//  * bwd_prep_kernel: D_i and L_i * log2(e) per query row, written in 32-row blocks
+//    [L (32 floats), D (32 floats)]; rows past Tq hold L = +inf and D = 0, so their recomputed
+//    probabilities are exactly 0.
+//  * bwd_dq_kernel (query-block outer loop, like the forward): a lane owns a query row and
+//    streams the K and V tiles of its head; per tile S^T and dP^T come from two MFMA products
+//    against Q^T and dO^T held in registers, dS is formed on the VALU, and dQ^T += K^T dS^T
+//    reads the same K tile transposed.
+//  * bwd_dkdv_kernel (key-block outer loop): a lane owns a key and holds K^T and V^T in
+//    registers; it streams the Q, dO and (L, D) tiles of every query head of its group, forms S
+//    and dP, then dV^T += dO^T P and dK^T += Q^T dS. dK and dV of a key are accumulated in
+//    registers over all the query heads that share it, so GQA needs no reduction pass.
+// The split recomputes S and dP once per kernel (7 products instead of 5) in exchange for no
+// atomic accumulation of dQ: the first page above notes that the usual key-outer order adds dQ
+// with atomics and is therefore not reproducible run to run, and that a deterministic mode pays
+// for reproducibility.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "lds_tiles.h"
+
+namespace fattn {
+namespace {
+
+using namespace lds;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2eF = 1.44269504088896340736f;
+constexpr float kPosInf = __builtin_inff();
+
+// ---- D_i = sum_d dO[i, d] * O[i, d] and L_i * log2(e), per 32-row block of every head.
+// D / 8 lanes read a row (16 bytes each) and reduce across themselves.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ O,
+                                                       const __bf16* __restrict__ dO,
+                                                       const float* __restrict__ LSE,
+                                                       float* __restrict__ ws, int BH, int Tq,
+                                                       int nqt) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  const long long r = (long long)blockIdx.x * RPB + tid / LPR;  // over BH * nqt * 32 rows
+  const int rows_per_head = nqt * 32;
+  const int bh = (int)(r / rows_per_head);
+  const int i = (int)(r - (long long)bh * rows_per_head);
+  const bool valid = bh < BH && i < Tq;
+  float acc = 0.f;
+  if (valid) {
+    const size_t e = ((size_t)bh * Tq + i) * D + 8 * sub;
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + e);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + e);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc = fmaf((float)o[k], (float)g[k], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (sub == 0 && bh < BH) {
+    float* blk = ws + ((size_t)bh * nqt + i / 32) * 64;
+    blk[i % 32] = valid ? LSE[(size_t)bh * Tq + i] * kLog2eF : kPosInf;
+    blk[32 + i % 32] = valid ? acc : 0.f;
+  }
+}
+
+// Workgroup order shared by both gradient kernels: workgroups are dealt round-robin to the 8
+// XCDs, so give each XCD a contiguous range of the logical order (the blocks of one head then
+// share that XCD's L2).
+__device__ __forceinline__ int xcd_order(int lin, int total) {
+  const int xcd = lin & 7, k = lin >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  return xcd * q8 + (xcd < r8 ? xcd : r8) + k;
+}
+
+// ---- dQ: one workgroup per (batch, query head, block of 32 * NW query rows).
+template <int D, int BC, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dQ, int Hq,
+    int Hkv, int Tq, int Tk, int causal, int window, float scale, float c) {
+  using S = Shape<D, BC, NW>;
+  __shared__ __align__(1024) unsigned char k_st0[S::TILE], k_st1[S::TILE];
+  __shared__ __align__(1024) unsigned char v_st0[S::TILE], v_st1[S::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hf = lane >> 5;
+
+  const int nqb = (Tq + S::BR - 1) / S::BR;
+  const int lin = xcd_order(blockIdx.x, gridDim.x);
+  const int bh = lin / nqb;
+  int qb = lin - bh * nqb;
+  if (causal) qb = nqb - 1 - qb;  // longest causal blocks first
+  const int b = bh / Hq;
+  const int h = bh - b * Hq;
+  const int g = h / (Hq / Hkv);
+  const int off = Tk - Tq;
+  const int nqt = (Tq + 31) / 32;
+
+  const __bf16* Qh = Q + (size_t)bh * Tq * D;
+  const __bf16* dOh = dO + (size_t)bh * Tq * D;
+  const __bf16* Kh = K + ((size_t)b * Hkv + g) * (size_t)Tk * D;
+  const __bf16* Vh = V + ((size_t)b * Hkv + g) * (size_t)Tk * D;
+
+  // key tiles: the same ranges as the forward pass of this query block
+  const int i0 = qb * S::BR;
+  const int q_end = min(i0 + S::BR, Tq);
+  const int kv_end = causal ? min(Tk, q_end + off) : Tk;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  int jm = Tk / BC;
+  if (causal) jm = min(jm, (i0 + off + 1) / BC);
+  jm = min(jm, ntiles);
+  const int kv_beg = window > 0 ? max(0, i0 + off - window + 1) : 0;
+  const int j_lo = kv_beg / BC;
+  const int j_ul = window > 0 ? (max(0, q_end - 1 + off - window + 1) + BC - 1) / BC : 0;
+  auto clean = [&](int j) { return j >= j_ul && j < jm; };
+
+  // ---- this lane's query row: Q^T and dO^T operands, L and D
+  const int qw0 = i0 + 32 * wave;
+  const int qrow = qw0 + col;
+  const bool wave_has_rows = qw0 < Tq;
+  const int wave_last = min(qw0 + 31, Tq - 1);
+  bf16x8 qb8[D / 16], ob8[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 rq = {0u, 0u, 0u, 0u}, ro = {0u, 0u, 0u, 0u};
+    if (qrow < Tq) {
+      rq = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * kk + 8 * hf);
+      ro = *reinterpret_cast<const u32x4*>(dOh + (size_t)qrow * D + 16 * kk + 8 * hf);
+    }
+    qb8[kk] = __builtin_bit_cast(bf16x8, rq);
+    ob8[kk] = __builtin_bit_cast(bf16x8, ro);
+  }
+  float Lr = kPosInf, Dr = 0.f;
+  if (qrow < Tq) {
+    const float* blk = ws + ((size_t)bh * nqt + qrow / 32) * 64;
+    Lr = blk[qrow % 32];
+    Dr = blk[32 + qrow % 32];
+  }
+
+  int dvo[S::NI_W];
+#pragma unroll
+  for (int i = 0; i < S::NI_W; ++i) {
+    const int q = wave + i * NW;
+    const int r = q * S::RPI + lane / S::C;
+    dvo[i] = r * S::RB + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
+  }
+  const int ka = rowbase<D, BC, NW>(col) ^ (hf << 4);
+  const int vq = lane >> 5, vg = (lane >> 4) & 1, ve = (lane >> 2) & 3, va = lane & 3;
+  int vab[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr)
+    vab[rr] = (rowbase<D, BC, NW>(8 * rr + 4 * vq + ve) ^ ((2 * vg + (va >> 1)) << 4)) + 8 * (va & 1);
+
+  // tile rows (keys) x this lane's row, against a register operand
+  auto rows_x = [&](f32x16 (&s)[BC / 32], const unsigned char* st, const bf16x8 (&op)[D / 16]) {
+#pragma unroll
+    for (int t = 0; t < BC / 32; ++t) {
+      s[t] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = *(const LDS_AS bf16x8*)(st + ((ka ^ (kk << 5)) + 32 * t * S::RB));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[kk], s[t], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+
+  auto active = [&](int j) {
+    return wave_has_rows && (!causal || j * BC <= wave_last + off) &&
+           (window == 0 || (j + 1) * BC - 1 >= qw0 + off - window + 1);
+  };
+
+  auto compute = [&](int j, const unsigned char* kst, const unsigned char* vst) {
+    f32x16 s[BC / 32], dp[BC / 32];
+    rows_x(s, kst, qb8);
+    rows_x(dp, vst, ob8);
+    const bool masked = !clean(j);
+    const int last = causal ? min(Tk - 1, qrow + off) : Tk - 1;
+    const int first = window > 0 ? qrow + off - window + 1 : 0;
+    bf16x8 ds[BC / 16];
+#pragma unroll
+    for (int ch = 0; ch < BC / 16; ++ch) {
+      const int t = ch >> 1, c2 = ch & 1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * c2 + i;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -Lr));
+        float v = p * (dp[t][r] - Dr);
+        if (masked) {
+          const int key = j * BC + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (key > last || key < first) v = 0.f;
+        }
+        ds[ch][i] = (__bf16)v;
+      }
+    }
+    // dQ^T += K^T dS^T: the K tile read transposed
+#pragma unroll
+    for (int ch = 0; ch < BC / 16; ++ch)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(kst + ((vab[0] ^ (dt << 6)) + 16 * ch * S::RB)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(kst + ((vab[1] ^ (dt << 6)) + 16 * ch * S::RB)));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ds[ch], acc[dt], 0, 0, 0);
+      }
+  };
+
+  // Stages start cleared: a stage row past Tk is then zero or a finite leftover of an earlier
+  // tile, and meets a zero dS.
+  for (int i = tid; i < S::TILE / 16; i += S::NT) {
+    *(LDS_AS u32x4*)(k_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    *(LDS_AS u32x4*)(k_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    *(LDS_AS u32x4*)(v_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    *(LDS_AS u32x4*)(v_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  if (j_lo < ntiles) {
+    dma_tile<D, BC, NW>(Kh, j_lo * BC, Tk, k_st0, wave, dvo);
+    dma_tile<D, BC, NW>(Vh, j_lo * BC, Tk, v_st0, wave, dvo);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto step = [&](int j, const unsigned char* k_cur, const unsigned char* v_cur,
+                  unsigned char* k_nxt, unsigned char* v_nxt) {
+    if (j + 1 < ntiles) {
+      dma_tile<D, BC, NW>(Kh, (j + 1) * BC, Tk, k_nxt, wave, dvo);
+      dma_tile<D, BC, NW>(Vh, (j + 1) * BC, Tk, v_nxt, wave, dvo);
+    }
+    if (active(j)) compute(j, k_cur, v_cur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  int j = j_lo;
+  for (; j + 1 < ntiles; j += 2) {
+    step(j, k_st0, v_st0, k_st1, v_st1);
+    step(j + 1, k_st1, v_st1, k_st0, v_st0);
+  }
+  if (j < ntiles) step(j, k_st0, v_st0, k_st1, v_st1);
+
+  if (qrow >= Tq) return;
+  __bf16* row = dQ + ((size_t)bh * Tq + qrow) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * dt + 8 * g4 + 4 * hf;
+      u32x2 packed = {pack2_bf16(acc[dt][4 * g4 + 0] * scale, acc[dt][4 * g4 + 1] * scale),
+                      pack2_bf16(acc[dt][4 * g4 + 2] * scale, acc[dt][4 * g4 + 3] * scale)};
+      *reinterpret_cast<u32x2*>(row + d0) = packed;
+    }
+}
+
+// ---- dK, dV: one workgroup per (batch, kv head, block of 32 * NW keys); the loop runs over the
+// query heads of the group and, in each, over the query tiles of BC rows that see a key of the
+// block.
+template <int D, int BC, int NW, int MINW>
+__global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dK,
+    __bf16* __restrict__ dV, int Hq, int Hkv, int Tq, int Tk, int causal, int window, float scale,
+    float c) {
+  using S = Shape<D, BC, NW>;
+  constexpr int BK = 32 * NW;     // keys per workgroup
+  constexpr int LWB = BC / 32;    // (L, D) blocks per query tile
+  static_assert(LWB <= NW, "one wave per (L, D) block");
+  __shared__ __align__(1024) unsigned char q_st0[S::TILE], q_st1[S::TILE];
+  __shared__ __align__(1024) unsigned char o_st0[S::TILE], o_st1[S::TILE];
+  __shared__ __align__(16) float lw_st0[64 * LWB], lw_st1[64 * LWB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hf = lane >> 5;
+
+  const int nkb = (Tk + BK - 1) / BK;
+  const int lin = xcd_order(blockIdx.x, gridDim.x);
+  const int bg = lin / nkb;
+  const int kb = lin - bg * nkb;  // ascending: the longest causal blocks first
+  const int b = bg / Hkv;
+  const int g = bg - b * Hkv;
+  const int G = Hq / Hkv;
+  const int off = Tk - Tq;
+  const int nqt = (Tq + 31) / 32;
+
+  const int k0 = kb * BK;
+  const int kw0 = k0 + 32 * wave;
+  const int kcol = kw0 + col;
+  const int k_last = min(Tk - 1, k0 + BK - 1);
+  const __bf16* Kh = K + (size_t)bg * Tk * D;
+  const __bf16* Vh = V + (size_t)bg * Tk * D;
+
+  // ---- this lane's key: K^T and V^T operands
+  bf16x8 kb8[D / 16], vb8[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
+    if (kcol < Tk) {
+      rk = *reinterpret_cast<const u32x4*>(Kh + (size_t)kcol * D + 16 * kk + 8 * hf);
+      rv = *reinterpret_cast<const u32x4*>(Vh + (size_t)kcol * D + 16 * kk + 8 * hf);
+    }
+    kb8[kk] = __builtin_bit_cast(bf16x8, rk);
+    vb8[kk] = __builtin_bit_cast(bf16x8, rv);
+  }
+
+  // ---- query rows that see a key of this block: causal rows from k0 - off on; under a window
+  // rows up to k_last + window - 1 - off
+  const int i_lo = causal ? max(0, k0 - off) : 0;
+  const int i_hi = window > 0 ? min(Tq - 1, k_last + window - 1 - off) : Tq - 1;
+  const int t_lo = i_lo / BC;
+  const int ntq = i_lo <= i_hi ? i_hi / BC - t_lo + 1 : 0;
+  const int nsteps = G * ntq;
+
+  int dvo[S::NI_W];
+#pragma unroll
+  for (int i = 0; i < S::NI_W; ++i) {
+    const int q = wave + i * NW;
+    const int r = q * S::RPI + lane / S::C;
+    dvo[i] = r * S::RB + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
+  }
+  const int ka = rowbase<D, BC, NW>(col) ^ (hf << 4);
+  const int vq = lane >> 5, vg = (lane >> 4) & 1, ve = (lane >> 2) & 3, va = lane & 3;
+  int vab[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr)
+    vab[rr] = (rowbase<D, BC, NW>(8 * rr + 4 * vq + ve) ^ ((2 * vg + (va >> 1)) << 4)) + 8 * (va & 1);
+
+  // Q, dO and (L, D) tiles of step s (query head g*G + s / ntq, query tile t_lo + s % ntq)
+  auto issue = [&](int s, unsigned char* qst, unsigned char* ost, float* lw) {
+    const int hh = g * G + s / ntq;
+    const int q0 = (t_lo + s % ntq) * BC;
+    const size_t bh = (size_t)b * Hq + hh;
+    dma_tile<D, BC, NW>(Q + bh * Tq * D, q0, Tq, qst, wave, dvo);
+    dma_tile<D, BC, NW>(dO + bh * Tq * D, q0, Tq, ost, wave, dvo);
+    if (wave < LWB) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(ws + bh * nqt * 64), (short)0, nqt * 256, kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lw + 64 * wave), 4,
+                                               (q0 / 32 + wave) * 256 + 4 * lane, 0, 0, 0);
+    }
+  };
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+
+  // tile rows (queries) x this lane's key, against a register operand
+  auto rows_x = [&](f32x16 (&s)[BC / 32], const unsigned char* st, const bf16x8 (&op)[D / 16]) {
+#pragma unroll
+    for (int t = 0; t < BC / 32; ++t) {
+      s[t] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = *(const LDS_AS bf16x8*)(st + ((ka ^ (kk << 5)) + 32 * t * S::RB));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[kk], s[t], 0, 0, 0);
+      }
+    }
+  };
+  // acc^T += tile^T x (bf16 operand whose k index runs over the tile rows)
+  auto tr_x = [&](f32x16 (&a)[D / 32], const bf16x8 (&pb)[BC / 16], const unsigned char* st) {
+#pragma unroll
+    for (int ch = 0; ch < BC / 16; ++ch)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(st + ((vab[0] ^ (dt << 6)) + 16 * ch * S::RB)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS i16x4*)(st + ((vab[1] ^ (dt << 6)) + 16 * ch * S::RB)));
+        const bf16x8 m = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        a[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(m, pb[ch], a[dt], 0, 0, 0);
+      }
+  };
+
+  auto compute = [&](int s, const unsigned char* qst, const unsigned char* ost, const float* lw) {
+    const int q0 = (t_lo + s % ntq) * BC;
+    if (kw0 >= Tk || (causal && q0 + BC - 1 + off < kw0) ||
+        (window > 0 && q0 + off - window + 1 > kw0 + 31))
+      return;  // no row of the tile sees a key of this wave
+    const bool masked = q0 + BC > Tq || (causal && q0 + off < kw0 + 31) ||
+                        (window > 0 && q0 + BC - 1 + off - window + 1 > kw0);
+    f32x16 sc[BC / 32], dp[BC / 32];
+    rows_x(sc, qst, kb8);
+    rows_x(dp, ost, vb8);
+    bf16x8 pb[BC / 16], db[BC / 16];
+#pragma unroll
+    for (int ch = 0; ch < BC / 16; ++ch) {
+      const int t = ch >> 1, c2 = ch & 1;
+      // rows 32t + 16c2 + 4hf + {0..3} and 32t + 16c2 + 8 + 4hf + {0..3} of the tile
+      const float* lb = lw + 64 * t + 16 * c2 + 4 * hf;
+      const f32x4 l0 = *(const LDS_AS f32x4*)(lb), l1 = *(const LDS_AS f32x4*)(lb + 8);
+      const f32x4 d0 = *(const LDS_AS f32x4*)(lb + 32), d1 = *(const LDS_AS f32x4*)(lb + 40);
+      const float Lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      const float Dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * c2 + i;
+        float p = __builtin_amdgcn_exp2f(fmaf(sc[t][r], c, -Lv[i]));
+        float v = p * (dp[t][r] - Dv[i]);
+        if (masked) {
+          const int row = q0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool vis = row < Tq && (!causal || kcol <= row + off) &&
+                           (window == 0 || kcol >= row + off - window + 1);
+          if (!vis) {
+            p = 0.f;
+            v = 0.f;
+          }
+        }
+        pb[ch][i] = (__bf16)p;
+        db[ch][i] = (__bf16)v;
+      }
+    }
+    tr_x(dv, pb, ost);  // dV^T += dO^T P
+    tr_x(dk, db, qst);  // dK^T += Q^T dS
+  };
+
+  // Stages start cleared (see the dQ kernel).
+  for (int i = tid; i < S::TILE / 16; i += S::NT) {
+    *(LDS_AS u32x4*)(q_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    *(LDS_AS u32x4*)(q_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    *(LDS_AS u32x4*)(o_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    *(LDS_AS u32x4*)(o_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  if (nsteps > 0) issue(0, q_st0, o_st0, lw_st0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  auto step = [&](int s, const unsigned char* q_cur, const unsigned char* o_cur,
+                  const float* lw_cur, unsigned char* q_nxt, unsigned char* o_nxt, float* lw_nxt) {
+    if (s + 1 < nsteps) issue(s + 1, q_nxt, o_nxt, lw_nxt);
+    compute(s, q_cur, o_cur, lw_cur);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  };
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    step(s, q_st0, o_st0, lw_st0, q_st1, o_st1, lw_st1);
+    step(s + 1, q_st1, o_st1, lw_st1, q_st0, o_st0, lw_st0);
+  }
+  if (s < nsteps) step(s, q_st0, o_st0, lw_st0, q_st1, o_st1, lw_st1);
+
+  if (kcol >= Tk) return;
+  __bf16* krow = dK + ((size_t)bg * Tk + kcol) * D;
+  __bf16* vrow = dV + ((size_t)bg * Tk + kcol) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * dt + 8 * g4 + 4 * hf;
+      u32x2 pk = {pack2_bf16(dk[dt][4 * g4 + 0] * scale, dk[dt][4 * g4 + 1] * scale),
+                  pack2_bf16(dk[dt][4 * g4 + 2] * scale, dk[dt][4 * g4 + 3] * scale)};
+      u32x2 pv = {pack2_bf16(dv[dt][4 * g4 + 0], dv[dt][4 * g4 + 1]),
+                  pack2_bf16(dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3])};
+      *reinterpret_cast<u32x2*>(krow + d0) = pk;
+      *reinterpret_cast<u32x2*>(vrow + d0) = pv;
+    }
+}
+
+template <int D>
+hipError_t launch_d(const BwdProblem& p, float* ws, hipStream_t stream) {
+  const int BH = p.B * p.Hq;
+  const int nqt = (p.Tq + 31) / 32;
+  const float c = p.scale * kLog2eF;
+  const __bf16* Q = static_cast<const __bf16*>(p.Q);
+  const __bf16* K = static_cast<const __bf16*>(p.K);
+  const __bf16* V = static_cast<const __bf16*>(p.V);
+  const __bf16* dO = static_cast<const __bf16*>(p.dO);
+
+  constexpr int RPB = 256 / (D / 8);
+  const long long rows = (long long)BH * nqt * 32;
+  bwd_prep_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(
+      static_cast<const __bf16*>(p.O), dO, p.LSE, ws, BH, p.Tq, nqt);
+
+  constexpr int DQ_NW = 8, DQ_BC = 32;
+  const int nqb = (p.Tq + 32 * DQ_NW - 1) / (32 * DQ_NW);
+  bwd_dq_kernel<D, DQ_BC, DQ_NW><<<dim3((unsigned)(BH * nqb)), dim3(64 * DQ_NW), 0, stream>>>(
+      Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal, p.window,
+      p.scale, c);
+
+  constexpr int KV_NW = 4, KV_BC = 32, KV_MINW = D >= 128 ? 1 : 2;
+  const int nkb = (p.Tk + 32 * KV_NW - 1) / (32 * KV_NW);
+  bwd_dkdv_kernel<D, KV_BC, KV_NW, KV_MINW>
+      <<<dim3((unsigned)(p.B * p.Hkv * nkb)), dim3(64 * KV_NW), 0, stream>>>(
+          Q, K, V, dO, ws, static_cast<__bf16*>(p.dK), static_cast<__bf16*>(p.dV), p.Hq, p.Hkv,
+          p.Tq, p.Tk, p.causal, p.window, p.scale, c);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_bf16(const BwdProblem& p, float* ws, hipStream_t stream) {
+  switch (p.d) {
+    case 32: return launch_d<32>(p, ws, stream);
+    case 64: return launch_d<64>(p, ws, stream);
+    case 128: return launch_d<128>(p, ws, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fattn

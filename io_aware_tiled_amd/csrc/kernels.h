@@ -40,4 +40,31 @@ hipError_t launch_prefill_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const Problem& p, int k0, int splits, int chunk, float* ws_o,
                               float* ws_lse, hipStream_t stream);
 
+// Host-side view of one backward problem (bf16 tensors, fp32 LSE). Layouts as the forward:
+// Q, O, dO, dQ [B, Hq, Tq, d]; K, V, dK, dV [B, Hkv, Tk, d]; LSE [B, Hq, Tq].
+struct BwdProblem {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* LSE;
+  void* dQ;
+  void* dK;
+  void* dV;
+  int B, Hq, Hkv, Tq, Tk, d;
+  int causal;
+  int window;   // as in Problem
+  float scale;  // signed softmax scale
+};
+
+// Floats of backward workspace: (L, D) in 32-row blocks for every (batch, query head).
+inline size_t backward_workspace_floats(int B, int Hq, int Tq) {
+  return (size_t)B * Hq * (size_t)((Tq + 31) / 32) * 64;
+}
+
+// bf16 backward: the (L, D) kernel, then the dQ and the dK/dV kernels, on `stream`.
+// ws holds backward_workspace_floats(B, Hq, Tq) floats. d in {32, 64, 128}.
+hipError_t launch_backward_bf16(const BwdProblem& p, float* ws, hipStream_t stream);
+
 }  // namespace fattn

@@ -30,10 +30,13 @@ from .attention import (  # noqa: F401
     tiled_head,
 )
 from .backward import (  # noqa: F401
+    backward_cols,
     backward_flops,
+    backward_rows,
     dense_backward,
     dense_backward_head,
     loss_gradient_fd,
+    tiled_backward,
     tiled_backward_head,
 )
 from . import accounting  # noqa: F401

@@ -118,6 +118,31 @@ def tiled_backward_head(q, k, v, o, lse, do, causal: bool, scale: Optional[float
     return dQ, dK, dV
 
 
+def tiled_backward(Q, K, V, O, LSE, dO, causal: bool, scale: Optional[float] = None,
+                   block_q: int = 64, block_kv: int = 64, window: Optional[int] = None):
+    """``tiled_backward_head`` over [B, Hq, Tq, d] with grouped kv heads, from given O and LSE.
+
+    This is the backward as the pages define its interface: (Q, K, V, O, L, dO) in, gradients
+    out, with P recomputed from L. A kv head's dK and dV add over the query heads that read it.
+    Returns (dQ [B, Hq, Tq, d], dK [B, Hkv, Tk, d], dV [B, Hkv, Tk, d]).
+    """
+    Q, K, V, O, LSE, dO = (np.asarray(x) for x in (Q, K, V, O, LSE, dO))
+    B, Hq, Tq, d = Q.shape
+    Hkv, Tk = K.shape[1], K.shape[2]
+    dQ = np.zeros((B, Hq, Tq, d))
+    dK = np.zeros((B, Hkv, Tk, d))
+    dV = np.zeros((B, Hkv, Tk, d))
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            gq, gk, gv = tiled_backward_head(Q[b, h], K[b, g], V[b, g], O[b, h], LSE[b, h],
+                                             dO[b, h], causal, scale, block_q, block_kv, window)
+            dQ[b, h] = gq
+            dK[b, g] += gk
+            dV[b, g] += gv
+    return dQ, dK, dV
+
+
 def loss_gradient_fd(q, k, v, do, causal: bool, which: str, idx, scale: Optional[float] = None,
                      eps: float = 1e-5, window: Optional[int] = None) -> float:
     """Central difference of sum(dO * O) with respect to one element of q, k or v.
@@ -140,6 +165,59 @@ def loss_gradient_fd(q, k, v, do, causal: bool, which: str, idx, scale: Optional
     return (fp - fm) / (2 * eps)
 
 
+def backward_rows(q, k, v, do, rows, causal: bool, scale: Optional[float] = None,
+                  window: Optional[int] = None) -> np.ndarray:
+    """dQ of the given query rows of one head, each row by the definition.
+
+    For row i: P_i and O_i from ``dense_head`` (the materialised softmax row), D_i = dO_i . O_i,
+    dP_i = dO_i V^T, dS_i = P_i * (dP_i - D_i), dQ_i = scale * dS_i K (the chain rule of
+    ``dense_backward_head``, one row at a time). Returns [len(rows), d].
+    """
+    from .attention import dense_head
+
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    sc = _default_scale(q.shape[1], scale)
+    idx = np.asarray(rows, dtype=np.int64)
+    O, _, P = dense_head(q, k, v, causal, scale, rows=idx, return_p=True, window=window)
+    D = np.sum(do[idx] * O, axis=1)
+    dP = do[idx] @ v.T
+    dS = P * (dP - D[:, None])
+    return sc * (dS @ k)
+
+
+def backward_cols(q, k, v, do, keys, causal: bool, scale: Optional[float] = None,
+                  window: Optional[int] = None, row_chunk: int = 1024):
+    """dK and dV of the given keys of one (query) head, by recomputation from L.
+
+    O and L of every query row come from ``dense_head`` (row chunks of ``row_chunk`` only bound
+    the memory; each row is the definition). Then, as in the pages' backward (P_ij = exp(S_ij -
+    L_i), "Efficient attention & KV cache", section 2.2), for the key columns j:
+    P_:j = exp(scale Q k_j - L) (0 where masked), dV_j = P_:j^T dO, dP_:j = dO v_j,
+    dS_:j = P_:j * (dP_:j - D), dK_j = scale dS_:j^T Q, with D = rowsum(dO * O).
+    Returns (dK [len(keys), d], dV [len(keys), d]) of this query head alone; a kv head's
+    gradient is the sum over the query heads that read it.
+    """
+    from .attention import dense_head
+
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    Tq, d = q.shape
+    Tk = k.shape[0]
+    sc = _default_scale(d, scale)
+    O = np.empty((Tq, d))
+    L = np.empty(Tq)
+    for r0 in range(0, Tq, row_chunk):
+        rr = np.arange(r0, min(r0 + row_chunk, Tq))
+        O[rr], L[rr] = dense_head(q, k, v, causal, scale, rows=rr, window=window)
+    D = np.sum(do * O, axis=1)
+    kk = np.asarray(keys, dtype=np.int64)
+    hide = _mask(Tq, Tk, causal, window)[:, kk]
+    P = np.where(hide, 0.0, np.exp(np.where(hide, 0.0, sc * (q @ k[kk].T)) - L[:, None]))
+    dV = P.T @ do
+    dS = P * (do @ v[kk].T - D[:, None])
+    dK = sc * (dS.T @ q)
+    return dK, dV
+
+
 def backward_flops(B: int, Hq: int, Tq: int, Tk: int, d: int, causal: bool) -> float:
     """Matmul FLOPs of the backward's five products (S, dP, dV, dK, dQ): 10 B Hq Tq Tk d, halved
     under a causal mask (the forward's convention for its two products, 4 B H T^2 d)."""
@@ -147,6 +225,7 @@ def backward_flops(B: int, Hq: int, Tq: int, Tk: int, d: int, causal: bool) -> f
     return f / 2.0 if causal else f
 
 
-__all__ = ["dense_backward_head", "dense_backward", "tiled_backward_head", "loss_gradient_fd",
-           "backward_flops"]
+__all__ = ["dense_backward_head", "dense_backward", "tiled_backward_head", "tiled_backward",
+           "loss_gradient_fd",
+           "backward_rows", "backward_cols", "backward_flops"]
 

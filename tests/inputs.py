@@ -12,6 +12,8 @@ Recipe (every tensor is reproducible slice by slice):
   * ``k_spike=(frac, factor)`` multiplies round(frac*T) K rows per (b, kv-head), chosen without
     replacement by ``default_rng([seed, 3, b, h])``, by ``factor`` before rounding (factor 8 is exact
     in both fp32 and bf16);
+  * the upstream gradient dO of a backward case: slice [Tq, d] at (b, h) from
+    ``default_rng([seed, 4, b, h])``, N(0, 1) whatever ``dist`` is, rounded like Q;
   * bf16 tensors are the float32 draws rounded to nearest-even; the oracle reads those same rounded
     values, widened exactly to float64.
 """
@@ -81,6 +83,7 @@ CONFIGS = {
 }
 
 Q_ID, K_ID, V_ID = 0, 1, 2
+SPIKE_ID, DO_ID = 3, 4
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -114,7 +117,7 @@ def head_slice(cfg: AttnConfig, which: int, b: int, h: int) -> np.ndarray:
         frac, factor = cfg.k_spike
         n = int(round(frac * T))
         if n > 0:
-            pick = np.random.default_rng([cfg.seed, 3, b, h]).choice(T, size=n, replace=False)
+            pick = np.random.default_rng([cfg.seed, SPIKE_ID, b, h]).choice(T, size=n, replace=False)
             x[pick] *= np.float32(factor)
     if cfg.dtype == "bf16":
         x = round_to_bf16(x)
@@ -133,6 +136,22 @@ def make_inputs(cfg: AttnConfig):
             K[b, h] = head_slice(cfg, K_ID, b, h)
             V[b, h] = head_slice(cfg, V_ID, b, h)
     return Q, K, V
+
+
+def grad_slice(cfg: AttnConfig, b: int, h: int) -> np.ndarray:
+    """One [Tq, d] float32 slice of the upstream gradient dO (rounded when the config is bf16)."""
+    x = np.random.default_rng([cfg.seed, DO_ID, b, h]).standard_normal((cfg.Tq, cfg.d),
+                                                                      dtype=np.float32)
+    return round_to_bf16(x) if cfg.dtype == "bf16" else x
+
+
+def make_grad(cfg: AttnConfig) -> np.ndarray:
+    """The upstream gradient dO [B, Hq, Tq, d] of a backward case."""
+    dO = np.empty((cfg.B, cfg.Hq, cfg.Tq, cfg.d), np.float32)
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            dO[b, h] = grad_slice(cfg, b, h)
+    return dO
 
 
 def to_torch(x: np.ndarray, dtype: str, device=None):

@@ -105,3 +105,49 @@ def test_key_gradients_sum_to_zero(causal):
 def test_backward_flops_convention():
     assert oracle.backward_flops(1, 32, 8192, 8192, 128, True) == 10 * 32 * 8192 ** 2 * 128 / 2
     assert oracle.backward_flops(2, 4, 100, 50, 64, False) == 10 * 2 * 4 * 100 * 50 * 64
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 6)])
+@pytest.mark.parametrize("Tq,Tk", [(40, 40), (23, 57)])
+def test_sampled_rows_and_columns_equal_dense(causal, window, Tq, Tk):
+    # The sampled forms used at large sizes agree with the dense backward on every row / key.
+    d = 8
+    q, k, v, do = _rand((Tq, d), 21), _rand((Tk, d), 22), _rand((Tk, d), 23), _rand((Tq, d), 24)
+    dQ, dK, dV, *_ = oracle.dense_backward_head(q, k, v, do, causal, 0.45, window)
+    rows = list(range(Tq))
+    assert np.max(np.abs(oracle.backward_rows(q, k, v, do, rows, causal, 0.45, window) - dQ)) \
+        <= 1e-12
+    keys = [0, 1, Tk // 3, Tk - 2, Tk - 1]
+    sK, sV = oracle.backward_cols(q, k, v, do, keys, causal, 0.45, window, row_chunk=7)
+    assert np.max(np.abs(sK - dK[keys])) <= 1e-12
+    assert np.max(np.abs(sV - dV[keys])) <= 1e-12
+
+
+def test_sampled_columns_against_finite_differences():
+    # An independent pin of the column form: central differences of sum(dO * O).
+    Tq, Tk, d = 11, 19, 5
+    q, k, v, do = _rand((Tq, d), 31), _rand((Tk, d), 32), _rand((Tk, d), 33), _rand((Tq, d), 34)
+    sK, sV = oracle.backward_cols(q, k, v, do, [2, 17], True, 0.8, 9, row_chunk=4)
+    for i, j in enumerate([2, 17]):
+        for c in (0, 3):
+            assert abs(oracle.loss_gradient_fd(q, k, v, do, True, "k", (j, c), 0.8, window=9)
+                       - sK[i, c]) < 1e-7
+            assert abs(oracle.loss_gradient_fd(q, k, v, do, True, "v", (j, c), 0.8, window=9)
+                       - sV[i, c]) < 1e-7
+    sQ = oracle.backward_rows(q, k, v, do, [0, 10], True, 0.8, 9)
+    for i, r in enumerate([0, 10]):
+        assert abs(oracle.loss_gradient_fd(q, k, v, do, True, "q", (r, 1), 0.8, window=9)
+                   - sQ[i, 1]) < 1e-7
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 4)])
+def test_batched_tiled_backward_equals_dense_with_gqa(causal, window):
+    B, Hq, Hkv, Tq, Tk, d = 2, 6, 2, 19, 30, 4
+    rng = np.random.default_rng(41)
+    Q = rng.standard_normal((B, Hq, Tq, d)); K = rng.standard_normal((B, Hkv, Tk, d))
+    V = rng.standard_normal((B, Hkv, Tk, d)); dO = rng.standard_normal((B, Hq, Tq, d))
+    O, L = oracle.dense_attention(Q, K, V, causal, 0.7, window=window)
+    ref = oracle.dense_backward(Q, K, V, dO, causal, 0.7, window)
+    got = oracle.tiled_backward(Q, K, V, O, L, dO, causal, 0.7, 8, 5, window)
+    for a, b in zip(got, ref):
+        assert np.max(np.abs(a - b)) <= 1e-12
