@@ -13,8 +13,9 @@ halved for the causal mask; the decode rate is reported as algorithmic HBM bytes
 
 After the timed steps, and outside them: the library's two probes (matrix-core rate on
 register operands, nontemporal HBM read rate) give the achievable rates the two kernels are also
-quoted against, and the sliding-window variants of both calls (window 4096) are timed, with the
-work of the visible (query, key) pairs only. One JSON line is printed.
+quoted against, the sliding-window variants of both calls (window 4096) are timed, with the
+work of the visible (query, key) pairs only, and so is the backward of the prefill call
+(attn_bwd, seeded upstream gradient), at 10*B*H*T^2*d/2 FLOPs. One JSON line is printed.
 
     python bench.py --calibrate-copy BYTES
 
@@ -65,6 +66,13 @@ def window_pairs(T, W):
 def window_decode_bytes(B, Hq, Hkv, W, d, eb=2):
     """A decode step under a window reads only the last W keys and values."""
     return decode_bytes(B, Hq, Hkv, W, d, eb)
+
+
+def backward_flops(B, H, Tq, Tk, d, causal):
+    """The backward's five products (S, dP, dV, dK, dQ): 10*B*H*Tq*Tk*d, halved under a causal
+    mask, the forward's convention for its two."""
+    f = 10.0 * B * H * Tq * Tk * d
+    return f / 2 if causal else f
 
 
 def stats_ms(times):
@@ -137,6 +145,17 @@ def device_inputs(cfg, torch):
 
     return (build(inputs.Q_ID, cfg.Hq, cfg.Tq), build(inputs.K_ID, cfg.Hkv, cfg.Tk),
             build(inputs.V_ID, cfg.Hkv, cfg.Tk))
+
+
+def device_grad(cfg, torch):
+    """The seeded upstream gradient dO of a backward case, on the GPU."""
+    from tests import inputs
+
+    t = torch.empty((cfg.B, cfg.Hq, cfg.Tq, cfg.d), dtype=torch.bfloat16, device="cuda")
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            t[b, h].copy_(inputs.to_torch(inputs.grad_slice(cfg, b, h), "bf16"))
+    return t
 
 
 def traffic_for(kernel_source, key):
@@ -290,6 +309,21 @@ def main():
     sw_bytes = window_decode_bytes(dc.B, dc.Hq, dc.Hkv, W, dc.d)
     sw_gbs = sw_bytes / (sw_d["median"] * 1e-3) / 1e9
 
+    # ---- the backward of the prefill call (O and LSE of the last forward call above)
+    print("[bench] backward", file=sys.stderr, flush=True)
+    fa.attn_fwd(q3, k3, v3, causal=pc.causal, scale=pc.scale, out=o3, lse=l3)
+    do3 = device_grad(pc, torch)
+    dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
+    bw = stats_ms(time_calls(torch, lambda: fa.attn_bwd(q3, k3, v3, o3, l3, do3, causal=pc.causal,
+                                                       scale=pc.scale, dq=dq3, dk=dk3, dv=dv3),
+                             10, 20))
+    if not all(bool(torch.isfinite(t).all()) for t in (dq3, dk3, dv3)):
+        print("non-finite gradient", file=sys.stderr)
+        sys.exit(1)
+    bw_flops = backward_flops(pc.B, pc.Hq, pc.Tq, pc.Tk, pc.d, pc.causal)
+    bw_tflops = bw_flops / (bw["median"] * 1e-3) / 1e12
+    del do3, dq3, dk3, dv3
+
     cpu = None
     if args.cpu_baseline == "auto":
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -344,6 +378,15 @@ def main():
                        "work": "K and V of the last 4096 keys read once, Q read, O and LSE "
                                "written",
                        "traffic": traffic_for("decode_bf16.hip", "decode_window")},
+        },
+        "backward": {
+            "workload": "backward of the causal prefill bf16 B=1 H=32 T=8192 d=128",
+            "ms": round(bw["median"], 4), "tflops": round(bw_tflops, 2),
+            "pct_mfma_peak": round(100 * bw_tflops / PEAK_BF16_TFLOPS, 2),
+            "flops_per_call": bw_flops, "ms_stats": _r(bw),
+            "work": "10*B*H*T^2*d/2: the five products S, dP, dV, dK, dQ; the kernels run seven "
+                    "(S and dP once in the dQ kernel and once in the dK/dV kernel)",
+            "traffic": traffic_for("backward_bf16.hip", "backward"),
         },
         "cpu_baseline": cpu,
     }

@@ -70,10 +70,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const __bf16* slice,
 }
 
 // One K or V tile, global -> LDS by direct-to-LDS loads: this wave's share of the 1 KB loads.
+// dvo[i] (i < NI_W) is this lane's LDS byte offset within the tile for the wave's i-th load.
 // (A device function rather than a lambda: the builtin exists only in the device pass.)
 template <int D, int BC, int NW>
 __device__ __forceinline__ void dma_tile(const __bf16* head, int j0, int Tk, unsigned char* dst,
-                                         int wave, const int (&dvo)[Shape<D, BC, NW>::NI_W]) {
+                                         int wave, const int* dvo) {
   using S = Shape<D, BC, NW>;
   const __amdgpu_buffer_rsrc_t rs = rows_rsrc<D>(head, j0, Tk);
 #pragma unroll

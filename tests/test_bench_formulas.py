@@ -26,3 +26,13 @@ def test_window_pairs(T, W):
 def test_window_decode_bytes_read_only_the_window():
     assert bench.window_decode_bytes(64, 64, 8, 4096, 128) == acc.decode_bytes(64, 64, 8, 4096,
                                                                                128)
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 8192, 8192, 128, True), (2, 8, 300, 300, 64, False)])
+def test_backward_flops(shape):
+    import oracle
+
+    assert bench.backward_flops(*shape) == oracle.backward_flops(*shape)
+    B, H, Tq, Tk, d, causal = shape
+    # five products against the forward's two: 2.5 times the forward count
+    assert bench.backward_flops(*shape) == 2.5 * bench.prefill_flops(B, H, Tq, Tk, d, causal)
