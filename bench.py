@@ -14,8 +14,10 @@ halved for the causal mask; the decode rate is reported as algorithmic HBM bytes
 After the timed steps, and outside them: the library's two probes (matrix-core rate on
 register operands, nontemporal HBM read rate) give the achievable rates the two kernels are also
 quoted against, the sliding-window variants of both calls (window 4096) are timed, with the
-work of the visible (query, key) pairs only, and so is the backward of the prefill call
-(attn_bwd, seeded upstream gradient), at 10*B*H*T^2*d/2 FLOPs. One JSON line is printed.
+work of the visible (query, key) pairs only, the decode call over a paged copy of its cache
+(attn_fwd_paged, 16-position pages in a random order; checked bitwise equal to the contiguous
+result), and the backward of the prefill call (attn_bwd, seeded upstream gradient), at
+10*B*H*T^2*d/2 FLOPs. One JSON line is printed.
 
     python bench.py --calibrate-copy BYTES
 
@@ -309,6 +311,37 @@ def main():
     sw_bytes = window_decode_bytes(dc.B, dc.Hq, dc.Hkv, W, dc.d)
     sw_gbs = sw_bytes / (sw_d["median"] * 1e-3) / 1e9
 
+    # ---- the decode call over a paged cache: the same keys and values in 16-position pages,
+    # dealt to physical blocks in a seeded random order
+    print("[bench] paged decode", file=sys.stderr, flush=True)
+    BS = 16
+    mb = dc.Tk // BS
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(dc.seed)
+    perm = torch.randperm(dc.B * mb, generator=gen).to("cuda")
+    def paged(x):
+        blocks = x.view(dc.B, dc.Hkv, mb, BS, dc.d).permute(0, 2, 1, 3, 4)
+        c = torch.empty((dc.B * mb, dc.Hkv, BS, dc.d), dtype=x.dtype, device="cuda")
+        c[perm] = blocks.reshape(dc.B * mb, dc.Hkv, BS, dc.d)
+        return c
+    kc4, vc4 = paged(k4), paged(v4)
+    table4 = perm.view(dc.B, mb).to(torch.int32).contiguous()
+    lens4 = torch.full((dc.B,), dc.Tk, dtype=torch.int32, device="cuda")
+    q4p, o4p = q4[:, :, 0].contiguous(), torch.empty(dc.B, dc.Hq, dc.d, dtype=torch.bfloat16,
+                                                     device="cuda")
+    l4p = torch.empty(dc.B, dc.Hq, device="cuda")
+    pg = stats_ms(time_calls(torch, lambda: fa.attn_fwd_paged(q4p, kc4, vc4, table4, lens4,
+                                                             scale=dc.scale, out=o4p, lse=l4p),
+                             10, 20))
+    fa.attn_fwd(q4, k4, v4, causal=dc.causal, scale=dc.scale, out=o4, lse=l4)
+    torch.cuda.synchronize()
+    if not torch.equal(o4p.view(torch.int16), o4[:, :, 0].view(torch.int16)):
+        print("paged decode differs from the contiguous decode", file=sys.stderr)
+        sys.exit(1)
+    pg_bytes = dbytes + 4 * dc.B * mb + 4 * dc.B  # plus the block table and lengths
+    pg_gbs = pg_bytes / (pg["median"] * 1e-3) / 1e9
+    del kc4, vc4
+
     # ---- the backward of the prefill call (O and LSE of the last forward call above)
     print("[bench] backward", file=sys.stderr, flush=True)
     fa.attn_fwd(q3, k3, v3, causal=pc.causal, scale=pc.scale, out=o3, lse=l3)
@@ -378,6 +411,16 @@ def main():
                        "work": "K and V of the last 4096 keys read once, Q read, O and LSE "
                                "written",
                        "traffic": traffic_for("decode_bf16.hip", "decode_window")},
+        },
+        "paged_decode": {
+            "workload": "GQA decode bf16 B=64 Hq=64 Hkv=8 Tk=8192 d=128 over a paged cache, "
+                        "16 positions per page, pages in a seeded random order",
+            "ms": round(pg["median"], 4), "gbs": round(pg_gbs, 1),
+            "pct_hbm_peak": round(100 * pg_gbs / PEAK_HBM_GBS, 2),
+            "bytes_per_call": pg_bytes, "ms_stats": _r(pg),
+            "work": "the contiguous decode's bytes plus the block table and lengths",
+            "bitwise_equal_to_contiguous": True,
+            "traffic": traffic_for("decode_bf16.hip", "decode_paged"),
         },
         "backward": {
             "workload": "backward of the causal prefill bf16 B=1 H=32 T=8192 d=128",

@@ -126,6 +126,43 @@ int attn_fwd_window_cfg(const void* Q, const void* K, const void* V, void* O, fl
                         int dtype, void* stream, const fattn_cfg_t* cfg);
 
 /*
+ * attn_fwd_paged: one decode step (one query token per sequence) over a paged KV cache
+ * ("Efficient attention & KV cache", section 2.5 and the interview question on what
+ * PagedAttention changes in the attention kernel: keys and values live in fixed-size blocks
+ * located through a per-sequence block table, and the kernel gathers each block from its
+ * physical location instead of reading one contiguous slice).
+ *
+ *   Q            [B, Hq, d]                          bf16
+ *   K_cache,
+ *   V_cache      [num_blocks, Hkv, block_size, d]    bf16; physical block n holds, for every kv
+ *                                                    head, block_size consecutive positions
+ *   block_table  [B, max_blocks_per_seq]             int32; entry (b, i) is the physical block
+ *                                                    holding positions i*block_size ..
+ *                                                    (i+1)*block_size - 1 of sequence b
+ *   seq_lens     [B]                                 int32; cached positions of sequence b
+ *   O            [B, Hq, d] bf16 and LSE [B, Hq] float32 (written)
+ *
+ * Sequence b attends, without a mask, to its positions 0 .. seq_lens[b] - 1 (the decode case of
+ * attn_fwd with Tq = 1): O and LSE equal attn_fwd on the gathered contiguous cache. GQA as in
+ * attn_fwd. All pointers are caller-owned device pointers on the current device; the tensors
+ * must be 16-byte aligned, block_table and seq_lens 4-byte aligned.
+ *
+ * Errors (host-side, before any HIP call): FATTN_ERR_INVALID for a NULL pointer, a misaligned
+ * pointer, block_size not a power of two in [16, 4096], num_blocks or max_blocks_per_seq < 1,
+ * max_blocks_per_seq * block_size above 2^31 - 1, and the shape errors of attn_fwd;
+ * FATTN_ERR_UNSUPPORTED for d not in {32, 64, 128} or dtype FATTN_F32. B == 0 or Hq == 0 is a
+ * no-op. The device-side contents are the caller's contract: seq_lens[b] is clamped to
+ * [0, max_blocks_per_seq * block_size]; a sequence of length 0 gets O = 0 and LSE = -inf; a
+ * table entry outside [0, num_blocks) is never dereferenced (its positions read as zero keys and
+ * values). Shares the split-K decode kernels and workspace of attn_fwd; the split plan covers
+ * max_blocks_per_seq * block_size keys.
+ */
+int attn_fwd_paged(const void* Q, const void* K_cache, const void* V_cache,
+                   const int* block_table, const int* seq_lens, void* O, float* LSE, int B,
+                   int Hq, int Hkv, int d, int num_blocks, int block_size, int max_blocks_per_seq,
+                   float scale, int dtype, void* stream);
+
+/*
  * attn_bwd: enqueue the backward pass of attn_fwd (or attn_fwd_window) on `stream`: the
  * gradients of a scalar loss with respect to Q, K and V, given its gradient dO with respect to
  * O. The probabilities are recomputed tile by tile from Q, K and the saved LSE instead of being

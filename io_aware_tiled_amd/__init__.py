@@ -75,6 +75,8 @@ lib.attn_fwd_window.argtypes = _FWD_ARGS
 lib.attn_fwd_window.restype = _i
 lib.attn_fwd_window_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
 lib.attn_fwd_window_cfg.restype = _i
+lib.attn_fwd_paged.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp]
+lib.attn_fwd_paged.restype = _i
 lib.attn_bwd.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _vp]
 lib.attn_bwd.restype = _i
 lib.attn_fwd_plan.argtypes = [_i] * 8 + [ctypes.POINTER(FattnCfg), ctypes.POINTER(FattnCfg)]
@@ -266,3 +268,58 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
     if rc != FATTN_OK:
         raise FattnError(rc, fattn_last_error())
     return dq, dk, dv
+
+
+def attn_fwd_paged_raw(Q, K_cache, V_cache, block_table, seq_lens, O, LSE, B, Hq, Hkv, d,
+                       num_blocks, block_size, max_blocks_per_seq, scale, dtype, stream) -> int:
+    """The C call attn_fwd_paged with plain integers for pointers; returns the status code."""
+    return lib.attn_fwd_paged(Q, K_cache, V_cache, block_table, seq_lens, O, LSE, B, Hq, Hkv, d,
+                              num_blocks, block_size, max_blocks_per_seq, scale, dtype, stream)
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale: Optional[float] = None,
+                   out=None, lse=None, stream=None):
+    """One decode step over a paged KV cache; returns (o [B, Hq, d], lse [B, Hq]).
+
+    q: [B, Hq, d] bfloat16; k_cache, v_cache: [num_blocks, Hkv, block_size, d] bfloat16;
+    block_table: [B, max_blocks] int32; seq_lens: [B] int32; all contiguous on the current device.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32, got {t.dtype}")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q must be [B, Hq, d], k_cache and v_cache [num_blocks, Hkv, bs, d]")
+    B, Hq, d = q.shape
+    num_blocks, Hkv, bs, dk_ = k_cache.shape
+    if dk_ != d:
+        raise ValueError("head dims differ")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = attn_fwd_paged_raw(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                            block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, Hq, Hkv, d, num_blocks, bs, block_table.shape[1],
+                            float(scale), FATTN_BF16, stream)
+    if rc != FATTN_OK:
+        raise FattnError(rc, fattn_last_error())
+    return out, lse

@@ -311,6 +311,75 @@ extern "C" int attn_fwd_window(const void* Q, const void* K, const void* V, void
                              stream, nullptr);
 }
 
+extern "C" int attn_fwd_paged(const void* Q, const void* K_cache, const void* V_cache,
+                              const int* block_table, const int* seq_lens, void* O, float* LSE,
+                              int B, int Hq, int Hkv, int d, int num_blocks, int block_size,
+                              int max_blocks_per_seq, float scale, int dtype, void* stream) {
+  g_last_error[0] = 0;
+  if (block_size < 16 || block_size > 4096 || (block_size & (block_size - 1)) != 0)
+    return fail(FATTN_ERR_INVALID, "block_size must be a power of two in [16, 4096]");
+  if (num_blocks < 1) return fail(FATTN_ERR_INVALID, "num_blocks must be >= 1");
+  if (max_blocks_per_seq < 1) return fail(FATTN_ERR_INVALID, "max_blocks_per_seq must be >= 1");
+  const long long max_keys = (long long)max_blocks_per_seq * block_size;
+  if (max_keys > 0x7fffffffLL) return fail(FATTN_ERR_INVALID, "max_blocks_per_seq too large");
+  if ((long long)num_blocks * Hkv * block_size * (d > 0 ? d : 1) > (1LL << 62))
+    return fail(FATTN_ERR_INVALID, "cache too large");
+  bool noop;
+  int rc = validate_shape(B, Hq, Hkv, 1, (int)max_keys, d, 0, dtype, &noop);
+  if (rc != FATTN_OK) return rc;
+  if (!std::isfinite(scale)) return fail(FATTN_ERR_INVALID, "scale is not finite");
+  if (noop) return FATTN_OK;
+  if (dtype != FATTN_BF16) return fail(FATTN_ERR_UNSUPPORTED, "paged decode is bf16 only");
+  if (!Q || !K_cache || !V_cache || !block_table || !seq_lens || !O || !LSE)
+    return fail(FATTN_ERR_INVALID, "NULL pointer");
+  if (!aligned16(Q) || !aligned16(K_cache) || !aligned16(V_cache) || !aligned16(O) ||
+      !aligned16(LSE))
+    return fail(FATTN_ERR_INVALID, "tensor pointer not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(FATTN_ERR_INVALID, "block_table or seq_lens not 4-byte aligned");
+  fattn_cfg_t plan;
+  rc = make_plan(B, Hq, Hkv, 1, (int)max_keys, d, 0, dtype, nullptr, &plan);
+  if (rc != FATTN_OK) return fail(rc, "launch configuration not implemented for this shape");
+
+  Problem p;
+  p.Q = Q;
+  p.K = K_cache;
+  p.V = V_cache;
+  p.O = O;
+  p.LSE = LSE;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Tq = 1;
+  p.Tk = (int)max_keys;
+  p.d = d;
+  p.causal = 0;
+  p.window = 0;
+  p.qsign = scale > 0.f ? 1 : (scale < 0.f ? -1 : 0);
+  p.abs_scale = scale == 0.f ? 1.f : std::fabs(scale);
+  p.log2_scale = p.abs_scale * kLog2e;
+  PagedKV pk;
+  pk.table = block_table;
+  pk.seq_lens = seq_lens;
+  pk.num_blocks = num_blocks;
+  pk.max_blocks = max_blocks_per_seq;
+  pk.bs_shift = 0;
+  while ((1 << pk.bs_shift) < block_size) ++pk.bs_shift;
+  const int chunk = ((int)((max_keys + plan.splits - 1) / plan.splits) + 31) / 32 * 32;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipGetDevice", he);
+  const size_t rows = (size_t)B * Hq * plan.splits;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  float* ws = nullptr;
+  rc = workspace(dev, s, rows * (size_t)d + rows, &ws);
+  if (rc != FATTN_OK) return rc;
+  he = launch_decode_paged_bf16(p, pk, plan.splits, chunk, ws, ws + rows * (size_t)d, s);
+  return he == hipSuccess ? FATTN_OK : hip_fail(FATTN_ERR_HIP, "kernel launch", he);
+}
+
 extern "C" int attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                         const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
                         int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window,

@@ -15,6 +15,11 @@
 // v_mfma_f32_16x16x32_bf16 (padded with zero rows when G < 16): S^T = K Q^T takes K straight
 // from global memory in the operand layout, and O^T = V^T P^T reads V^T from a small per-wave
 // LDS transpose whose key order matches the S^T accumulator, as in the prefill kernel.
+//
+// The same kernels serve a paged cache ("Efficient attention & KV cache", section 2.5 and the
+// interview question on what PagedAttention changes in the kernel): keys and values sit in
+// fixed-size pages located through a per-sequence block table, and the kernel fetches each
+// 16-key half of its 32-key blocks from the page the table names, one table read per half.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -43,12 +48,23 @@ struct Block {
   u32x4 v[8];          // V rows of keys 4gg+r and 16+4gg+r, dims 8dg .. 8dg+8
 };
 
+// Where the 16-key halves of a 32-key block live. Keys kb + 16h + r (r < 16) are rows
+// row[h] + r of the K and V bases; a half whose rows are not readable has ok[h] false.
+// Contiguous caches: the [Tk, D] slice of one (batch, kv head), row[h] = kb + 16h.
+// Paged caches [num_blocks, Hkv, bs, D] (bs a power of two >= 16, so a 16-key half never
+// crosses a page): row[h] = (page * Hkv + kv head) * bs + (kb + 16h) mod bs with page read from
+// the sequence's block table.
+struct Halves {
+  size_t row[2];
+  bool ok[2];
+};
+
 // One 32-key block of K and V into registers. Every key and value is read exactly once per
 // decode step, so the loads carry the nontemporal hint: they stream past the caches instead of
 // evicting lines that other wavefronts still use (measured: 5.8 -> 6.5 TB/s on the GQA shape).
 template <int D>
-__device__ __forceinline__ void load_block(Block<D>& blk, const __bf16* Kh, const __bf16* Vh,
-                                           int kb, int kend, int lane) {
+__device__ __forceinline__ void load_block(Block<D>& blk, const __bf16* Kb, const __bf16* Vb,
+                                           const Halves& hv, int kb, int kend, int lane) {
   const int c16 = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -56,9 +72,9 @@ __device__ __forceinline__ void load_block(Block<D>& blk, const __bf16* Kh, cons
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < kend)
-        x = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + 32 * c + 8 * g4));
+      if (key < kend && hv.ok[t])
+        x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            Kb + (hv.row[t] + c16) * D + 32 * c + 8 * g4));
       blk.k[t][c] = x;
     }
   }
@@ -66,20 +82,54 @@ __device__ __forceinline__ void load_block(Block<D>& blk, const __bf16* Kh, cons
     const int gg = lane & 3, dg = lane >> 2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int key = kb + 4 * gg + (i & 3) + 16 * (i >> 2);
+      const int h = i >> 2, r = 4 * gg + (i & 3);
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < kend)
-        x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + 8 * dg));
+      if (kb + 16 * h + r < kend && hv.ok[h])
+        x = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(Vb + (hv.row[h] + r) * D + 8 * dg));
       blk.v[i] = x;
     }
   }
 }
 
-template <int D>
+// Block-table view of one sequence of a paged cache (unused by contiguous launches).
+struct PageMap {
+  const int* table;  // this sequence's row of the block table
+  int nblocks;       // physical blocks in the cache; entries outside [0, nblocks) read as zeros
+  int Hkv, g;        // kv heads per page and this workgroup's kv head
+  int sh;            // log2(block size)
+};
+
+template <bool PAGED>
+__device__ __forceinline__ Halves halves_of(int kb, int kend, const PageMap& pm) {
+  Halves hv;
+  if (!PAGED) {
+    hv.row[0] = (size_t)kb;
+    hv.row[1] = (size_t)kb + 16;
+    hv.ok[0] = hv.ok[1] = true;
+    return hv;
+  }
+  const int mask = (1 << pm.sh) - 1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int key = kb + 16 * h;
+    const int page = key < kend ? pm.table[key >> pm.sh] : 0;
+    hv.ok[h] = key < kend && page >= 0 && page < pm.nblocks;
+    hv.row[h] = hv.ok[h] ? (((size_t)page * pm.Hkv + pm.g) << pm.sh) + (key & mask) : 0;
+  }
+  return hv;
+}
+
+// PAGED: K and V are paged caches [num_blocks, Hkv, bs, D] read through `table`
+// ([B, max_blocks] physical block ids) with seq_lens[b] keys for batch b (clamped to
+// max_blocks * bs); Tk and k0 are then unused. Otherwise K, V are [B, Hkv, Tk, D] and the keys
+// [k0, Tk) are read.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hq, int Hkv, int Tk, int k0,
-    int splits, int chunk, float log2_scale, int qsign) {
+    int splits, int chunk, float log2_scale, int qsign, const int* __restrict__ table,
+    const int* __restrict__ seq_lens, int max_blocks, int bs_shift, int nblocks) {
   __shared__ __align__(16) __bf16 Vt[D * VS];
 
   const int lane = threadIdx.x;
@@ -93,8 +143,15 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
   w /= nqg;
   const int hk = w % Hkv;
   const int b = w / Hkv;
+  PageMap pm = {nullptr, nblocks, Hkv, hk, bs_shift};
+  int kv_len = Tk;
+  if (PAGED) {
+    pm.table = table + (size_t)b * max_blocks;
+    kv_len = max(0, min(seq_lens[b], max_blocks << bs_shift));
+    k0 = 0;
+  }
   const int kbeg = k0 + s * chunk;  // k0 > 0: a sliding window starts at key Tk - window
-  const int kend = min(Tk, kbeg + chunk);
+  const int kend = min(kv_len, kbeg + chunk);
   const int qi = qg * 16 + c16;
   const bool qvalid = qi < G;
   const int hq = hk * G + qi;
@@ -111,8 +168,8 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
     qb[c] = __builtin_bit_cast(bf16x8, raw);
   }
 
-  const __bf16* Kh = K + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
-  const __bf16* Vh = V + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
+  const __bf16* Kh = PAGED ? K : K + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
+  const __bf16* Vh = PAGED ? V : V + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
 
   float M = kNegInf, lsum = 0.f;
   f32x4 acc[D / 16];
@@ -120,12 +177,13 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
   for (int mt = 0; mt < D / 16; ++mt) acc[mt] = f32x4{};
 
   Block<D> cur;
-  if (kbeg < kend) load_block<D>(cur, Kh, Vh, kbeg, kend, lane);
+  if (kbeg < kend) load_block<D>(cur, Kh, Vh, halves_of<PAGED>(kbeg, kend, pm), kbeg, kend, lane);
 
   for (int kb = kbeg; kb < kend; kb += KB) {
     const bool more = kb + KB < kend;
     Block<D> nxt;
-    if (more) load_block<D>(nxt, Kh, Vh, kb + KB, kend, lane);
+    if (more)
+      load_block<D>(nxt, Kh, Vh, halves_of<PAGED>(kb + KB, kend, pm), kb + KB, kend, lane);
 
     __syncthreads();  // the previous block's V^T reads are done
     if (lane < D / 2) {
@@ -220,8 +278,9 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
     tot += w;
     o = fmaf(w, ws_o[(row * splits + s) * D + d], o);
   }
-  O[row * D + d] = (__bf16)(o / tot);
-  if (d == 0) LSE[row] = base + logf(tot);
+  // no key at all (a paged sequence of length 0): O = 0, LSE = -inf
+  O[row * D + d] = (__bf16)(tot > 0.f ? o / tot : 0.f);
+  if (d == 0) LSE[row] = tot > 0.f ? base + logf(tot) : kNegInf;
 }
 
 template <int D>
@@ -233,10 +292,31 @@ hipError_t launch_t(const Problem& p, int k0, int splits, int chunk, float* ws_o
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL || (long long)p.B * p.Hq > 0x7fffffffLL)
     return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(decode_partial_kernel<D>, dim3((unsigned)grid), dim3(64), 0, stream,
-                     static_cast<const __bf16*>(p.Q), static_cast<const __bf16*>(p.K),
+  hipLaunchKernelGGL((decode_partial_kernel<D, false>), dim3((unsigned)grid), dim3(64), 0,
+                     stream, static_cast<const __bf16*>(p.Q), static_cast<const __bf16*>(p.K),
                      static_cast<const __bf16*>(p.V), ws_o, ws_lse, p.Hq, p.Hkv, p.Tk, k0,
-                     splits, chunk, p.log2_scale, p.qsign);
+                     splits, chunk, p.log2_scale, p.qsign, nullptr, nullptr, 0, 0, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(D), 0, stream,
+                     ws_o, ws_lse, static_cast<__bf16*>(p.O), p.LSE, splits);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_paged_t(const Problem& p, const PagedKV& pk, int splits, int chunk,
+                          float* ws_o, float* ws_lse, hipStream_t stream) {
+  const int G = p.Hq / p.Hkv;
+  const int nqg = (G + 15) / 16;
+  const long long grid = (long long)p.B * p.Hkv * nqg * splits;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL || (long long)p.B * p.Hq > 0x7fffffffLL)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_partial_kernel<D, true>), dim3((unsigned)grid), dim3(64), 0, stream,
+                     static_cast<const __bf16*>(p.Q), static_cast<const __bf16*>(p.K),
+                     static_cast<const __bf16*>(p.V), ws_o, ws_lse, p.Hq, p.Hkv, 0, 0, splits,
+                     chunk, p.log2_scale, p.qsign, pk.table, pk.seq_lens, pk.max_blocks,
+                     pk.bs_shift, pk.num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)(p.B * p.Hq)), dim3(D), 0, stream,
@@ -245,6 +325,16 @@ hipError_t launch_t(const Problem& p, int k0, int splits, int chunk, float* ws_o
 }
 
 }  // namespace
+
+hipError_t launch_decode_paged_bf16(const Problem& p, const PagedKV& pk, int splits, int chunk,
+                                    float* ws_o, float* ws_lse, hipStream_t stream) {
+  switch (p.d) {
+    case 32: return launch_paged_t<32>(p, pk, splits, chunk, ws_o, ws_lse, stream);
+    case 64: return launch_paged_t<64>(p, pk, splits, chunk, ws_o, ws_lse, stream);
+    case 128: return launch_paged_t<128>(p, pk, splits, chunk, ws_o, ws_lse, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_decode_bf16(const Problem& p, int k0, int splits, int chunk, float* ws_o,
                               float* ws_lse, hipStream_t stream) {

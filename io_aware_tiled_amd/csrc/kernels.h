@@ -40,6 +40,22 @@ hipError_t launch_prefill_f32(const Problem& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const Problem& p, int k0, int splits, int chunk, float* ws_o,
                               float* ws_lse, hipStream_t stream);
 
+// A paged KV cache: K and V are [num_blocks, Hkv, block_size, d]; table is [B, max_blocks]
+// physical block ids (int32), seq_lens [B] keys per sequence (int32); all device pointers.
+struct PagedKV {
+  const int* table;
+  const int* seq_lens;
+  int num_blocks;
+  int max_blocks;
+  int bs_shift;  // log2(block_size), block_size >= 16
+};
+
+// bf16 split-K decode over a paged cache: as launch_decode_bf16 with the keys of batch b read
+// through its block-table row; p.K and p.V are the cache bases, p.Tk is unused. The split plan
+// covers max_blocks * block_size keys; splits past a sequence's length write empty partials.
+hipError_t launch_decode_paged_bf16(const Problem& p, const PagedKV& pk, int splits, int chunk,
+                                    float* ws_o, float* ws_lse, hipStream_t stream);
+
 // Host-side view of one backward problem (bf16 tensors, fp32 LSE). Layouts as the forward:
 // Q, O, dO, dQ [B, Hq, Tq, d]; K, V, dK, dV [B, Hkv, Tk, d]; LSE [B, Hq, Tq].
 struct BwdProblem {

@@ -14,6 +14,11 @@ Recipe (every tensor is reproducible slice by slice):
     in both fp32 and bf16);
   * the upstream gradient dO of a backward case: slice [Tq, d] at (b, h) from
     ``default_rng([seed, 4, b, h])``, N(0, 1) whatever ``dist`` is, rounded like Q;
+  * a paged cache (``make_paged``) holds the K and V above for sequences of given lengths: the
+    logical blocks of all sequences are dealt to physical blocks in the order of a permutation
+    from ``default_rng([seed, 5])``, a few spare blocks and the tails of partly filled blocks hold
+    N(0, 1) filler that no visible position reads, and table entries past a sequence's last
+    block name arbitrary valid blocks;
   * bf16 tensors are the float32 draws rounded to nearest-even; the oracle reads those same rounded
     values, widened exactly to float64.
 """
@@ -83,7 +88,7 @@ CONFIGS = {
 }
 
 Q_ID, K_ID, V_ID = 0, 1, 2
-SPIKE_ID, DO_ID = 3, 4
+SPIKE_ID, DO_ID, PAGE_ID = 3, 4, 5
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -152,6 +157,36 @@ def make_grad(cfg: AttnConfig) -> np.ndarray:
         for h in range(cfg.Hq):
             dO[b, h] = grad_slice(cfg, b, h)
     return dO
+
+
+def make_paged(cfg: AttnConfig, block_size: int, seq_lens, spare: int = 3):
+    """A paged cache holding the K, V of ``cfg`` (Tk = the longest sequence) for sequences of the
+    given lengths. Returns (K_cache, V_cache [num_blocks, Hkv, block_size, d] float32,
+    block_table [B, max_blocks] int32, seq_lens [B] int32)."""
+    _, K, V = make_inputs(cfg)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    bs = int(block_size)
+    max_blocks = max(1, -(-cfg.Tk // bs))
+    need = [-(-int(n) // bs) for n in seq_lens]
+    num_blocks = sum(need) + spare
+    rng = np.random.default_rng([cfg.seed, PAGE_ID])
+    perm = rng.permutation(num_blocks)
+    shape = (num_blocks, cfg.Hkv, bs, cfg.d)
+    Kc = rng.standard_normal(shape, dtype=np.float32)
+    Vc = rng.standard_normal(shape, dtype=np.float32)
+    if cfg.dtype == "bf16":
+        Kc, Vc = round_to_bf16(Kc), round_to_bf16(Vc)
+    table = rng.integers(0, num_blocks, size=(cfg.B, max_blocks)).astype(np.int32)
+    n = 0
+    for b in range(cfg.B):
+        for i in range(need[b]):
+            blk = int(perm[n])
+            n += 1
+            table[b, i] = blk
+            rows = min(bs, int(seq_lens[b]) - i * bs)
+            Kc[blk, :, :rows] = K[b, :, i * bs:i * bs + rows]
+            Vc[blk, :, :rows] = V[b, :, i * bs:i * bs + rows]
+    return Kc, Vc, table, seq_lens
 
 
 def to_torch(x: np.ndarray, dtype: str, device=None):
