@@ -14,7 +14,8 @@ halved for the causal mask; the decode rate is reported as algorithmic HBM bytes
 After the timed steps, and outside them: the library's two probes (matrix-core rate on
 register operands, nontemporal HBM read rate) give the achievable rates the two kernels are also
 quoted against, the sliding-window variants of both calls (window 4096) are timed, with the
-work of the visible (query, key) pairs only, the decode call over a paged copy of its cache
+work of the visible (query, key) pairs only, a packed batch of variable-length documents (attn_fwd_varlen, 32768 tokens), the decode call over
+a paged copy of its cache
 (attn_fwd_paged, 16-position pages in a random order; checked bitwise equal to the contiguous
 result), and the backward of the prefill call (attn_bwd, seeded upstream gradient), at
 10*B*H*T^2*d/2 FLOPs. One JSON line is printed.
@@ -75,6 +76,23 @@ def backward_flops(B, H, Tq, Tk, d, causal):
     mask, the forward's convention for its two."""
     f = 10.0 * B * H * Tq * Tk * d
     return f / 2 if causal else f
+
+
+VARLEN_TOKENS = 32768
+VARLEN_SEED = 77
+
+
+def varlen_doc_lengths(total, lo, hi, seed):
+    """Document lengths drawn U[lo, hi] from the seed until they cover `total` tokens; the last
+    one is cut to fit."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    lens = []
+    while sum(lens) < total:
+        lens.append(int(rng.integers(lo, hi + 1)))
+    lens[-1] -= sum(lens) - total
+    return [x for x in lens if x > 0]
 
 
 def stats_ms(times):
@@ -252,6 +270,8 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
 
+    import numpy as np
+
     import io_aware_tiled_amd as fa
     from tests import inputs
 
@@ -342,6 +362,28 @@ def main():
     pg_gbs = pg_bytes / (pg["median"] * 1e-3) / 1e9
     del kc4, vc4
 
+    # ---- a packed training batch: 32768 tokens of documents with lengths U[128, 8192]
+    print("[bench] packed variable-length prefill", file=sys.stderr, flush=True)
+    lens = varlen_doc_lengths(VARLEN_TOKENS, 128, 8192, VARLEN_SEED)
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device="cuda")
+    gv = torch.Generator(device="cuda")
+    gv.manual_seed(VARLEN_SEED)
+    qv = torch.randn(VARLEN_TOKENS, pc.Hq, pc.d, device="cuda", generator=gv).to(torch.bfloat16)
+    kv = torch.randn(VARLEN_TOKENS, pc.Hkv, pc.d, device="cuda", generator=gv).to(torch.bfloat16)
+    vv = torch.randn(VARLEN_TOKENS, pc.Hkv, pc.d, device="cuda", generator=gv).to(torch.bfloat16)
+    ov = torch.empty_like(qv)
+    lv = torch.empty(pc.Hq, VARLEN_TOKENS, device="cuda")
+    vl = stats_ms(time_calls(torch, lambda: fa.attn_fwd_varlen(qv, kv, vv, cu, cu, max(lens),
+                                                              max(lens), causal=True,
+                                                              scale=pc.scale, out=ov, lse=lv),
+                             10, 20))
+    if not bool(torch.isfinite(ov).all()):
+        print("non-finite packed output", file=sys.stderr)
+        sys.exit(1)
+    vl_flops = sum(prefill_flops(1, pc.Hq, n, n, pc.d, True) for n in lens)
+    vl_tflops = vl_flops / (vl["median"] * 1e-3) / 1e12
+    del qv, kv, vv, ov, lv
+
     # ---- the backward of the prefill call (O and LSE of the last forward call above)
     print("[bench] backward", file=sys.stderr, flush=True)
     fa.attn_fwd(q3, k3, v3, causal=pc.causal, scale=pc.scale, out=o3, lse=l3)
@@ -411,6 +453,15 @@ def main():
                        "work": "K and V of the last 4096 keys read once, Q read, O and LSE "
                                "written",
                        "traffic": traffic_for("decode_bf16.hip", "decode_window")},
+        },
+        "varlen": {
+            "workload": f"causal packed batch bf16: {VARLEN_TOKENS} tokens in {len(lens)} "
+                        f"documents with lengths U[128, 8192] (seed {VARLEN_SEED}), H=32, d=128",
+            "ms": round(vl["median"], 4), "tflops": round(vl_tflops, 2),
+            "pct_mfma_peak": round(100 * vl_tflops / PEAK_BF16_TFLOPS, 2),
+            "flops_per_call": vl_flops, "ms_stats": _r(vl),
+            "work": "sum over documents of 4*H*L^2*d/2 (the causal count of each document)",
+            "traffic": traffic_for("prefill_bf16.hip", "prefill_varlen"),
         },
         "paged_decode": {
             "workload": "GQA decode bf16 B=64 Hq=64 Hkv=8 Tk=8192 d=128 over a paged cache, "

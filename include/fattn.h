@@ -126,6 +126,39 @@ int attn_fwd_window_cfg(const void* Q, const void* K, const void* V, void* O, fl
                         int dtype, void* stream, const fattn_cfg_t* cfg);
 
 /*
+ * attn_fwd_varlen: causal or full attention over a packed batch of sequences of different
+ * lengths, concatenated without padding and described by cumulative lengths, so that no score
+ * between two sequences is ever formed ("4.2 FlashAttention I: IO-Awareness & The Online
+ * Softmax", section "Practical use: you almost never write this yourself": the packed call with
+ * cumulative sequence offsets; "Efficient attention & KV cache", section 4, document masks
+ * through the variable-length interface for training).
+ *
+ *   Q, O          [total_q, Hq, d]  bf16 (O written)
+ *   K, V          [total_k, Hkv, d] bf16
+ *   LSE           [Hq, total_q]     float32 (written)
+ *   cu_seqlens_q  [num_seqs + 1]    int32 device array: sequence b owns query rows
+ *                                   cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1
+ *   cu_seqlens_k  [num_seqs + 1]    int32, the same for key/value rows
+ *
+ * Within sequence b everything is attn_fwd (or attn_fwd_window when window > 0) on its slices,
+ * with bottom-right causal alignment when its query and key lengths differ. max_seqlen_q and
+ * max_seqlen_k must be at least every sequence's lengths (rows past max_seqlen_q are not
+ * computed). Device-side contents are the caller's contract: offsets are clamped to
+ * [0, total]; a row that sees no key (a causal sequence with fewer keys than queries, or no
+ * keys) gets O = 0 and LSE = -inf. Pointers are caller-owned device pointers, tensors 16-byte
+ * aligned, cu arrays 4-byte aligned.
+ *
+ * Errors (host-side): FATTN_ERR_INVALID for NULL or misaligned pointers, negative sizes, Hq not a
+ * multiple of Hkv, causal not 0/1, a window without causal, a non-finite scale;
+ * FATTN_ERR_UNSUPPORTED for d not in {32, 64, 128} or dtype FATTN_F32. num_seqs == 0,
+ * Hq == 0 or total_q == 0 is a no-op.
+ */
+int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs, int total_q,
+                    int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d,
+                    int causal, int window, float scale, int dtype, void* stream);
+
+/*
  * attn_fwd_paged: one decode step (one query token per sequence) over a paged KV cache
  * ("Efficient attention & KV cache", section 2.5 and the interview question on what
  * PagedAttention changes in the attention kernel: keys and values live in fixed-size blocks

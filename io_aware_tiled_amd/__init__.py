@@ -75,6 +75,8 @@ lib.attn_fwd_window.argtypes = _FWD_ARGS
 lib.attn_fwd_window.restype = _i
 lib.attn_fwd_window_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
 lib.attn_fwd_window_cfg.restype = _i
+lib.attn_fwd_varlen.argtypes = [_vp] * 7 + [_i] * 10 + [_f, _i, _vp]
+lib.attn_fwd_varlen.restype = _i
 lib.attn_fwd_paged.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp]
 lib.attn_fwd_paged.restype = _i
 lib.attn_bwd.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _vp]
@@ -320,6 +322,66 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale: Optional[f
                             block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                             lse.data_ptr(), B, Hq, Hkv, d, num_blocks, bs, block_table.shape[1],
                             float(scale), FATTN_BF16, stream)
+    if rc != FATTN_OK:
+        raise FattnError(rc, fattn_last_error())
+    return out, lse
+
+
+def attn_fwd_varlen_raw(Q, K, V, O, LSE, cu_q, cu_k, num_seqs, total_q, total_k, max_q, max_k,
+                        Hq, Hkv, d, causal, window, scale, dtype, stream) -> int:
+    """The C call attn_fwd_varlen with plain integers for pointers; returns the status code."""
+    return lib.attn_fwd_varlen(Q, K, V, O, LSE, cu_q, cu_k, num_seqs, total_q, total_k, max_q,
+                               max_k, Hq, Hkv, d, causal, window, scale, dtype, stream)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    causal: bool = False, scale: Optional[float] = None,
+                    window: Optional[int] = None, out=None, lse=None, stream=None):
+    """Attention over a packed batch; returns (o [total_q, Hq, d], lse [Hq, total_q]).
+
+    q: [total_q, Hq, d]; k, v: [total_k, Hkv, d]; bfloat16, contiguous, on the current device.
+    cu_seqlens_q / cu_seqlens_k: int32 [num_seqs + 1] cumulative lengths on the device.
+    """
+    import torch
+
+    if window is not None and not causal:
+        raise ValueError("a sliding window is a causal mask: pass causal=True")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [total, H, d]")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise TypeError(f"{name} must be a 1-D int32 tensor")
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk_ = k.shape
+    if dk_ != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [total_k, Hkv, d] with q's d")
+    num_seqs = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != num_seqs + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = attn_fwd_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                             max(num_seqs, 0), total_q, total_k, int(max_seqlen_q),
+                             int(max_seqlen_k), Hq, Hkv, d, int(bool(causal)), int(window or 0),
+                             float(scale), FATTN_BF16, stream)
     if rc != FATTN_OK:
         raise FattnError(rc, fattn_last_error())
     return out, lse

@@ -311,6 +311,64 @@ extern "C" int attn_fwd_window(const void* Q, const void* K, const void* V, void
                              stream, nullptr);
 }
 
+extern "C" int attn_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                               int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                               int Hq, int Hkv, int d, int causal, int window, float scale,
+                               int dtype, void* stream) {
+  g_last_error[0] = 0;
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(FATTN_ERR_INVALID, "negative size");
+  if (window < 0) return fail(FATTN_ERR_INVALID, "window must be >= 0");
+  if (window > 0 && causal != 1) return fail(FATTN_ERR_INVALID, "a window needs causal = 1");
+  // Per-sequence lengths live on the device; shape checks use the longest ones. A causal row
+  // that sees no key (a sequence with fewer keys than queries) is not an error here.
+  const int tk_check = max_seqlen_k > max_seqlen_q ? max_seqlen_k : max_seqlen_q;
+  bool noop;
+  int rc = validate_shape(num_seqs, Hq, Hkv, max_seqlen_q, tk_check > 0 ? tk_check : 1, d,
+                          causal, dtype, &noop);
+  if (rc != FATTN_OK) return rc;
+  if (!std::isfinite(scale)) return fail(FATTN_ERR_INVALID, "scale is not finite");
+  if (noop || total_q == 0) return FATTN_OK;
+  if (dtype != FATTN_BF16) return fail(FATTN_ERR_UNSUPPORTED, "packed batches are bf16 only");
+  if ((long long)total_q * Hq * d > 0x7fffffffffffLL || (long long)total_k * Hkv * d > 0x7fffffffffffLL)
+    return fail(FATTN_ERR_INVALID, "packed tensors too large");
+  if ((long long)Hkv * d * 2 * 64 > 0x7fffffffLL) return fail(FATTN_ERR_INVALID, "Hkv * d too large");
+  if (!Q || !K || !V || !O || !LSE || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(FATTN_ERR_INVALID, "NULL pointer");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
+    return fail(FATTN_ERR_INVALID, "tensor pointer not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return fail(FATTN_ERR_INVALID, "cu_seqlens not 4-byte aligned");
+  if (window >= max_seqlen_k) window = 0;
+
+  Problem p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.LSE = LSE;
+  p.B = num_seqs;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Tq = max_seqlen_q;
+  p.Tk = max_seqlen_k;
+  p.d = d;
+  p.causal = causal;
+  p.window = window;
+  p.qsign = scale > 0.f ? 1 : (scale < 0.f ? -1 : 0);
+  p.abs_scale = scale == 0.f ? 1.f : std::fabs(scale);
+  p.log2_scale = p.abs_scale * kLog2e;
+  Packed pk;
+  pk.cu_q = cu_seqlens_q;
+  pk.cu_k = cu_seqlens_k;
+  pk.total_q = total_q;
+  pk.total_k = total_k;
+  hipError_t e = launch_prefill_varlen_bf16(p, pk, 3, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FATTN_OK : hip_fail(FATTN_ERR_HIP, "kernel launch", e);
+}
+
 extern "C" int attn_fwd_paged(const void* Q, const void* K_cache, const void* V_cache,
                               const int* block_table, const int* seq_lens, void* O, float* LSE,
                               int B, int Hq, int Hkv, int d, int num_blocks, int block_size,

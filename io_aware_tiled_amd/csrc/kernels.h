@@ -30,6 +30,21 @@ struct Problem {
 hipError_t launch_prefill_bf16(const Problem& p, int block_kv, int waves, int schedule,
                                hipStream_t stream);
 
+// A packed variable-length batch: sequence b owns rows cu_q[b] .. cu_q[b+1]-1 of the
+// [total_q, Hq, d] query tensor and rows cu_k[b] .. cu_k[b+1]-1 of the [total_k, Hkv, d] key and
+// value tensors (device int32 arrays of B + 1 entries).
+struct Packed {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+};
+
+// bf16 matrix-core prefill over a packed batch (64-key tiles, 8 waves): p.B is the number of
+// sequences, p.Tq and p.Tk the longest lengths (the grid covers p.Tq rows per sequence; longer
+// sequences are cut there), LSE is [Hq, total_q].
+hipError_t launch_prefill_varlen_bf16(const Problem& p, const Packed& pk, int schedule,
+                                      hipStream_t stream);
+
 // fp32 vector-ALU path, any Tq (also Tq == 1), d in {32, 64, 128}.
 hipError_t launch_prefill_f32(const Problem& p, hipStream_t stream);
 

@@ -86,6 +86,26 @@ __device__ __forceinline__ void dma_tile(const __bf16* head, int j0, int Tk, uns
   }
 }
 
+// One tile of rows j0 .. j0+BC-1 of a slice whose consecutive rows are row_elems elements apart
+// (row_elems >= D: packed [total, H, D] tensors), global -> LDS like dma_tile. dvo[i] must have
+// been computed with row stride row_elems * 2 bytes. Rows at or past T read as zeros.
+template <int D, int BC, int NW>
+__device__ __forceinline__ void dma_tile_strided(const __bf16* head, int j0, int T, int row_elems,
+                                                 unsigned char* dst, int wave, const int* dvo) {
+  using S = Shape<D, BC, NW>;
+  const int rows = min(T - j0, BC);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(head + (size_t)j0 * row_elems), (short)0,
+      rows > 0 ? ((rows - 1) * row_elems + D) * 2 : 0, kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < S::NI_W; ++i) {
+    const int q = wave + i * NW;
+    if (S::NI % NW == 0 || q < S::NI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + q * 1024), 16, dvo[i], 0,
+                                               0, 0);
+  }
+}
+
 // Values of lane l and lane l ^ 32 (the same query row in the other half-wave), via
 // v_permlane32_swap on two copies of x. Written as inline asm because the compiler folds the
 // two results of the builtin into one when both inputs are the same value.

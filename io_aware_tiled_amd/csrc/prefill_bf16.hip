@@ -44,11 +44,17 @@ using namespace lds;
 
 constexpr float kRebase = 8.0f;  // lazy re-base threshold, log2 units
 
-template <int D, int BC, int NW>
+// VARLEN: packed variable-length batch. Q, O are [total_q, Hq, D], K, V [total_k, Hkv, D] and
+// LSE [Hq, total_q]; sequence b owns query rows cu_q[b] .. cu_q[b+1]-1 and key rows
+// cu_k[b] .. cu_k[b+1]-1 (clamped to the totals), B is the number of sequences and Tq, Tk arrive
+// as the longest lengths the grid was sized for. Otherwise Q, O are [B, Hq, Tq, D], K, V
+// [B, Hkv, Tk, D] and LSE [B, Hq, Tq].
+template <int D, int BC, int NW, bool VARLEN>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Tq, int Tk,
-    int causal, int window, float log2_scale, int qsign, int schedule) {
+    int causal, int window, float log2_scale, int qsign, int schedule,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
   using S = Shape<D, BC, NW>;
   // One array per stage, so the compiler can tell a direct-to-LDS load into one stage from reads
   // of another and does not make those reads wait for the load.
@@ -72,17 +78,44 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     const int q8 = total >> 3, r8 = total & 7;
     lin = xcd * q8 + (xcd < r8 ? xcd : r8) + k;
   }
-  const int bh = lin / nqb;
+  int bh = lin / nqb;
   int qb = lin - bh * nqb;
   if (schedule == 2 && causal) qb = nqb - 1 - qb;  // longest causal blocks first
+  if (schedule == 3) {
+    // Query-block-major, longest causal blocks first across all (batch, head) pairs, dealt
+    // round-robin to the XCDs as dispatched: every XCD gets an even share of every block size.
+    // For packed batches, whose documents differ in length, where a head-contiguous range per
+    // XCD would give one XCD one document.
+    const int nbh = total / nqb;
+    bh = lin % nbh;
+    qb = lin / nbh;
+    if (causal) qb = nqb - 1 - qb;
+  }
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int g = h / (Hq / Hkv);
+  // packed batches: this sequence's rows and lengths (the documents do not see each other)
+  int q_begin = 0, k_begin = 0;
+  if constexpr (VARLEN) {
+    q_begin = min(max(cu_q[b], 0), total_q);
+    const int q_stop = min(max(cu_q[b + 1], q_begin), total_q);
+    k_begin = min(max(cu_k[b], 0), total_k);
+    const int k_stop = min(max(cu_k[b + 1], k_begin), total_k);
+    Tq = min(q_stop - q_begin, Tq);
+    Tk = min(k_stop - k_begin, Tk);
+    if (qb * S::BR >= Tq) return;  // the whole workgroup: past this sequence's rows
+  }
   const int off = Tk - Tq;
+  // elements between consecutive rows of one head
+  const size_t qstr = VARLEN ? (size_t)Hq * D : (size_t)D;
+  const size_t kstr = VARLEN ? (size_t)Hkv * D : (size_t)D;
 
-  const __bf16* Qh = Q + ((size_t)b * Hq + h) * (size_t)Tq * D;
-  const __bf16* Kh = K + ((size_t)b * Hkv + g) * (size_t)Tk * D;
-  const __bf16* Vh = V + ((size_t)b * Hkv + g) * (size_t)Tk * D;
+  const __bf16* Qh = VARLEN ? Q + ((size_t)q_begin * Hq + h) * D
+                            : Q + ((size_t)b * Hq + h) * (size_t)Tq * D;
+  const __bf16* Kh = VARLEN ? K + ((size_t)k_begin * Hkv + g) * D
+                            : K + ((size_t)b * Hkv + g) * (size_t)Tk * D;
+  const __bf16* Vh = VARLEN ? V + ((size_t)k_begin * Hkv + g) * D
+                            : V + ((size_t)b * Hkv + g) * (size_t)Tk * D;
 
   const int i0 = qb * S::BR;
   const int q_end = min(i0 + S::BR, Tq);
@@ -110,7 +143,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   for (int kk = 0; kk < D / 16; ++kk) {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (qrow < Tq && qsign != 0) {
-      raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * kk + 8 * hf);
+      raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * qstr + 16 * kk + 8 * hf);
       if (qsign < 0) raw ^= 0x80008000u;  // exact negation of both bf16 halves
     }
     qb8[kk] = __builtin_bit_cast(bf16x8, raw);
@@ -119,12 +152,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   // ---- per-lane constant offsets
   // direct-to-LDS loads: LDS slot `lane` of load q holds row q*RPI + lane/C, physical chunk
   // lane%C, i.e. logical chunk (lane%C) ^ swz(row) of that row
+  const int krb = VARLEN ? (int)(kstr * 2) : S::RB;  // bytes between K (V) rows in memory
   int dvo[S::NI_W];
 #pragma unroll
   for (int i = 0; i < S::NI_W; ++i) {
     const int q = wave + i * NW;
     const int r = q * S::RPI + lane / S::C;
-    dvo[i] = r * S::RB + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
+    dvo[i] = r * krb + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
   }
   // K operand of row col, chunk 2kk+hf: ka ^ (kk << 5), plus 32t rows for the t-th key half
   const int ka = rowbase<D, BC, NW>(col) ^ (hf << 4);
@@ -137,7 +171,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     vab[rr] = (rowbase<D, BC, NW>(8 * rr + 4 * vq + ve) ^ ((2 * vg + (va >> 1)) << 4)) + 8 * (va & 1);
 
   auto issue_tile = [&](const __bf16* head, int j0, unsigned char* dst) {
-    dma_tile<D, BC, NW>(head, j0, Tk, dst, wave, dvo);
+    if constexpr (VARLEN)
+      dma_tile_strided<D, BC, NW>(head, j0, Tk, (int)kstr, dst, wave, dvo);
+    else
+      dma_tile<D, BC, NW>(head, j0, Tk, dst, wave, dvo);
   };
 
   // S^T for one tile from a K stage
@@ -316,8 +353,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   halves(lsum, l_lo, l_hi);
   const float l = l_lo + l_hi;
   if (qrow >= Tq) return;
-  const float inv = 1.f / l;
-  __bf16* Orow = O + (((size_t)b * Hq + h) * (size_t)Tq + qrow) * D;
+  // a packed sequence can have rows that see no key (causal, fewer keys than queries, or none):
+  // O = 0 and LSE = -inf for them
+  const bool empty = VARLEN && !(l > 0.f);
+  const float inv = empty ? 0.f : 1.f / l;
+  __bf16* Orow = VARLEN ? O + ((size_t)(q_begin + qrow) * Hq + h) * D
+                        : O + (((size_t)b * Hq + h) * (size_t)Tq + qrow) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -328,44 +369,64 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
       *reinterpret_cast<u32x2*>(Orow + d0) = packed;
     }
   if (hf == 0) {
-    LSE[((size_t)b * Hq + h) * (size_t)Tq + qrow] = (M + __builtin_amdgcn_logf(l)) * kLn2;
+    const float lse = empty ? kNegInf : (M + __builtin_amdgcn_logf(l)) * kLn2;
+    if constexpr (VARLEN)
+      LSE[(size_t)h * total_q + q_begin + qrow] = lse;
+    else
+      LSE[((size_t)b * Hq + h) * (size_t)Tq + qrow] = lse;
   }
 }
 
-template <int D, int BC, int NW>
-hipError_t launch_t(const Problem& p, int schedule, hipStream_t stream) {
+template <int D, int BC, int NW, bool VARLEN>
+hipError_t launch_t(const Problem& p, int schedule, const Packed* pk, hipStream_t stream) {
   using S = Shape<D, BC, NW>;
   const int nqb = (p.Tq + S::BR - 1) / S::BR;
   const long long grid = (long long)p.B * p.Hq * nqb;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, NW>), dim3((unsigned)grid), dim3(S::NT), 0,
-                     stream, static_cast<const __bf16*>(p.Q),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, BC, NW, VARLEN>), dim3((unsigned)grid),
+                     dim3(S::NT), 0, stream, static_cast<const __bf16*>(p.Q),
                      static_cast<const __bf16*>(p.K), static_cast<const __bf16*>(p.V),
                      static_cast<__bf16*>(p.O), p.LSE, p.B, p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
-                     p.window, p.log2_scale, p.qsign, schedule);
+                     p.window, p.log2_scale, p.qsign, schedule, pk ? pk->cu_q : nullptr,
+                     pk ? pk->cu_k : nullptr, pk ? pk->total_q : 0, pk ? pk->total_k : 0);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const Problem& p, int block_kv, int waves, int schedule, hipStream_t stream) {
-  if (block_kv == 64 && waves == 4) return launch_t<D, 64, 4>(p, schedule, stream);
-  if (block_kv == 64 && waves == 8) return launch_t<D, 64, 8>(p, schedule, stream);
-  if (block_kv == 32 && waves == 4) return launch_t<D, 32, 4>(p, schedule, stream);
-  if (block_kv == 32 && waves == 8) return launch_t<D, 32, 8>(p, schedule, stream);
+hipError_t launch_d(const Problem& p, int block_kv, int waves, int schedule, const Packed* pk,
+                    hipStream_t stream) {
+  if (pk) {  // packed batches use one configuration per head dim
+    if (block_kv == 64 && waves == 8) return launch_t<D, 64, 8, true>(p, schedule, pk, stream);
+    return hipErrorInvalidValue;
+  }
+  if (block_kv == 64 && waves == 4) return launch_t<D, 64, 4, false>(p, schedule, pk, stream);
+  if (block_kv == 64 && waves == 8) return launch_t<D, 64, 8, false>(p, schedule, pk, stream);
+  if (block_kv == 32 && waves == 4) return launch_t<D, 32, 4, false>(p, schedule, pk, stream);
+  if (block_kv == 32 && waves == 8) return launch_t<D, 32, 8, false>(p, schedule, pk, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_any(const Problem& p, int block_kv, int waves, int schedule, const Packed* pk,
+                      hipStream_t stream) {
+  switch (p.d) {
+    case 32: return launch_d<32>(p, block_kv, waves, schedule, pk, stream);
+    case 64: return launch_d<64>(p, block_kv, waves, schedule, pk, stream);
+    case 128: return launch_d<128>(p, block_kv, waves, schedule, pk, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const Problem& p, int block_kv, int waves, int schedule,
                                hipStream_t stream) {
-  switch (p.d) {
-    case 32: return launch_d<32>(p, block_kv, waves, schedule, stream);
-    case 64: return launch_d<64>(p, block_kv, waves, schedule, stream);
-    case 128: return launch_d<128>(p, block_kv, waves, schedule, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_any(p, block_kv, waves, schedule, nullptr, stream);
+}
+
+hipError_t launch_prefill_varlen_bf16(const Problem& p, const Packed& pk, int schedule,
+                                      hipStream_t stream) {
+  return launch_any(p, 64, 8, schedule, &pk, stream);  // schedule 3 by default (api.cpp)
 }
 
 }  // namespace fattn

@@ -13,8 +13,8 @@ the five pages on tiled/online-softmax attention:
   * "Efficient attention & KV cache" (ML interview book).
 
 Parity status: every function below is pinned by `tests/test_oracle_pins.py`,
-`tests/test_window_pins.py`, `tests/test_backward_pins.py`, `tests/test_paged_pins.py` and
-`tests/test_accounting.py` against
+`tests/test_window_pins.py`, `tests/test_backward_pins.py`, `tests/test_paged_pins.py`,
+`tests/test_varlen_pins.py` and `tests/test_accounting.py` against
 values the pages print, closed forms, invariants, finite differences and library special cases.
 No function is "parity unpinned".
 """
@@ -41,4 +41,5 @@ from .backward import (  # noqa: F401
     tiled_backward_head,
 )
 from .paged import gather_sequence, paged_decode  # noqa: F401
+from .varlen import varlen_attention  # noqa: F401
 from . import accounting  # noqa: F401

@@ -19,6 +19,9 @@ Recipe (every tensor is reproducible slice by slice):
     from ``default_rng([seed, 5])``, a few spare blocks and the tails of partly filled blocks hold
     N(0, 1) filler that no visible position reads, and table entries past a sequence's last
     block name arbitrary valid blocks;
+  * a packed batch (``make_packed``) of documents with lengths (Lq_b, Lk_b): the rows of document b,
+    head h are ``head_slice`` of the config with Tq = Lq_b (Q) or Tk = Lk_b (K, V), laid out as
+    [total, H, d] with cumulative offsets;
   * bf16 tensors are the float32 draws rounded to nearest-even; the oracle reads those same rounded
     values, widened exactly to float64.
 """
@@ -187,6 +190,26 @@ def make_paged(cfg: AttnConfig, block_size: int, seq_lens, spare: int = 3):
             Kc[blk, :, :rows] = K[b, :, i * bs:i * bs + rows]
             Vc[blk, :, :rows] = V[b, :, i * bs:i * bs + rows]
     return Kc, Vc, table, seq_lens
+
+
+def make_packed(cfg: AttnConfig, lens_q, lens_k=None):
+    """Packed Q [total_q, Hq, d], K, V [total_k, Hkv, d] (float32) and int32 cumulative offsets
+    cu_q, cu_k [n + 1] for documents of the given lengths (lens_k defaults to lens_q)."""
+    lens_q = [int(x) for x in lens_q]
+    lens_k = lens_q if lens_k is None else [int(x) for x in lens_k]
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    Q = np.empty((int(cu_q[-1]), cfg.Hq, cfg.d), np.float32)
+    K = np.empty((int(cu_k[-1]), cfg.Hkv, cfg.d), np.float32)
+    V = np.empty((int(cu_k[-1]), cfg.Hkv, cfg.d), np.float32)
+    for b, (lq, lk) in enumerate(zip(lens_q, lens_k)):
+        c = cfg.replace(Tq=max(lq, 1), Tk=max(lk, 1))
+        for h in range(cfg.Hq):
+            Q[cu_q[b]:cu_q[b + 1], h] = head_slice(c, Q_ID, b, h)[:lq]
+        for h in range(cfg.Hkv):
+            K[cu_k[b]:cu_k[b + 1], h] = head_slice(c, K_ID, b, h)[:lk]
+            V[cu_k[b]:cu_k[b + 1], h] = head_slice(c, V_ID, b, h)[:lk]
+    return Q, K, V, cu_q, cu_k
 
 
 def to_torch(x: np.ndarray, dtype: str, device=None):

@@ -36,3 +36,11 @@ def test_backward_flops(shape):
     B, H, Tq, Tk, d, causal = shape
     # five products against the forward's two: 2.5 times the forward count
     assert bench.backward_flops(*shape) == 2.5 * bench.prefill_flops(B, H, Tq, Tk, d, causal)
+
+
+def test_varlen_document_lengths_cover_the_batch():
+    lens = bench.varlen_doc_lengths(bench.VARLEN_TOKENS, 128, 8192, bench.VARLEN_SEED)
+    assert sum(lens) == bench.VARLEN_TOKENS and all(1 <= n <= 8192 for n in lens)
+    # the work counted is each document's causal count, as the oracle's accounting has it
+    total = sum(bench.prefill_flops(1, 32, n, n, 128, True) for n in lens)
+    assert total == sum(acc.attention_flops(1, 32, n, n, 128, True) for n in lens)
