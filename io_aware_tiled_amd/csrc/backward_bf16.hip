@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.h"
 #include "lds_tiles.h"
@@ -191,24 +192,33 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     f32x16 s[BC / 32], dp[BC / 32];
     rows_x(s, kst, qb8);
     rows_x(dp, vst, ob8);
-    const bool masked = !clean(j);
-    const int last = causal ? min(Tk - 1, qrow + off) : Tk - 1;
-    const int first = window > 0 ? qrow + off - window + 1 : 0;
     bf16x8 ds[BC / 16];
+    // visible keys of the tile for this lane's row (relative to the tile start): key_lo..key_hi
+    const int j0 = j * BC;
+    const int key_hi = (causal ? min(Tk - 1, qrow + off) : Tk - 1) - j0;
+    const int key_lo = (window > 0 ? qrow + off - window + 1 : 0) - j0;
+    // two copies of the element loop, with and without the mask, so neither holds a branch
+    auto elements = [&](auto with_mask) {
 #pragma unroll
-    for (int ch = 0; ch < BC / 16; ++ch) {
-      const int t = ch >> 1, c2 = ch & 1;
+      for (int ch = 0; ch < BC / 16; ++ch) {
+        const int t = ch >> 1, c2 = ch & 1;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * c2 + i;
-        float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -Lr));
-        float v = p * (dp[t][r] - Dr);
-        if (masked) {
-          const int key = j * BC + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key > last || key < first) v = 0.f;
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * c2 + i;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -Lr));
+          float v = p * (dp[t][r] - Dr);
+          if constexpr (decltype(with_mask)::value) {
+            const int kk = 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+            v = (kk > key_hi || kk < key_lo) ? 0.f : v;
+          }
+          ds[ch][i] = (__bf16)v;
         }
-        ds[ch][i] = (__bf16)v;
       }
+    };
+    if (!clean(j)) {
+      elements(std::true_type{});
+    } else {
+      elements(std::false_type{});
     }
     // dQ^T += K^T dS^T: the K tile read transposed
 #pragma unroll
@@ -407,32 +417,43 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
     rows_x(sc, qst, kb8);
     rows_x(dp, ost, vb8);
     bf16x8 pb[BC / 16], db[BC / 16];
+    // visible rows of the tile for this lane's key (relative to q0); empty when row_hi < row_lo
+    const int row_lo = causal ? max(0, kcol - off - q0) : 0;
+    int row_hi = min(BC - 1, Tq - 1 - q0);
+    if (window > 0) row_hi = min(row_hi, kcol - off + window - 1 - q0);
+    // The element loop exists twice, with and without the mask, so that neither holds a branch:
+    // a uniform test inside an unrolled element loop splits it into many small blocks.
+    auto elements = [&](auto with_mask) {
 #pragma unroll
-    for (int ch = 0; ch < BC / 16; ++ch) {
-      const int t = ch >> 1, c2 = ch & 1;
-      // rows 32t + 16c2 + 4hf + {0..3} and 32t + 16c2 + 8 + 4hf + {0..3} of the tile
-      const float* lb = lw + 64 * t + 16 * c2 + 4 * hf;
-      const f32x4 l0 = *(const LDS_AS f32x4*)(lb), l1 = *(const LDS_AS f32x4*)(lb + 8);
-      const f32x4 d0 = *(const LDS_AS f32x4*)(lb + 32), d1 = *(const LDS_AS f32x4*)(lb + 40);
-      const float Lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-      const float Dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      for (int ch = 0; ch < BC / 16; ++ch) {
+        const int t = ch >> 1, c2 = ch & 1;
+        // rows 32t + 16c2 + 4hf + {0..3} and 32t + 16c2 + 8 + 4hf + {0..3} of the tile
+        const float* lb = lw + 64 * t + 16 * c2 + 4 * hf;
+        const f32x4 l0 = *(const LDS_AS f32x4*)(lb), l1 = *(const LDS_AS f32x4*)(lb + 8);
+        const f32x4 d0 = *(const LDS_AS f32x4*)(lb + 32), d1 = *(const LDS_AS f32x4*)(lb + 40);
+        const float Lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+        const float Dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * c2 + i;
-        float p = __builtin_amdgcn_exp2f(fmaf(sc[t][r], c, -Lv[i]));
-        float v = p * (dp[t][r] - Dv[i]);
-        if (masked) {
-          const int row = q0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool vis = row < Tq && (!causal || kcol <= row + off) &&
-                           (window == 0 || kcol >= row + off - window + 1);
-          if (!vis) {
-            p = 0.f;
-            v = 0.f;
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * c2 + i;
+          float p = __builtin_amdgcn_exp2f(fmaf(sc[t][r], c, -Lv[i]));
+          float v = p * (dp[t][r] - Dv[i]);
+          if constexpr (decltype(with_mask)::value) {
+            // rows row_lo .. row_hi of the query tile see this lane's key
+            const int rr = 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool vis = rr >= row_lo && rr <= row_hi;
+            p = vis ? p : 0.f;
+            v = vis ? v : 0.f;
           }
+          pb[ch][i] = (__bf16)p;
+          db[ch][i] = (__bf16)v;
         }
-        pb[ch][i] = (__bf16)p;
-        db[ch][i] = (__bf16)v;
       }
+    };
+    if (masked) {
+      elements(std::true_type{});
+    } else {
+      elements(std::false_type{});
     }
     tr_x(dv, pb, ost);  // dV^T += dO^T P
     tr_x(dk, db, qst);  // dK^T += Q^T dS
