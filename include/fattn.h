@@ -1,5 +1,6 @@
 /*
- * libfattn: fused attention forward pass for AMD Instinct MI355X (gfx950).
+ * libfattn: fused attention for AMD Instinct MI355X (gfx950): the forward pass (attn_fwd,
+ * attn_fwd_window, attn_fwd_varlen, attn_fwd_paged) and its backward (attn_bwd).
  *
  * Computes, for every batch b, query head h and query row i,
  *   O[b,h,i,:] = softmax_j(scale * Q[b,h,i,:] . K[b,g,j,:] + mask(i,j)) V[b,g,j,:]
@@ -79,8 +80,8 @@ typedef struct fattn_cfg {
  *   FATTN_ERR_UNSUPPORTED d not in {32, 64, 128}.
  * B == 0 or Tq == 0 (or Hq == 0) is a no-op that returns FATTN_OK.
  * A launch failure returns FATTN_ERR_HIP; device faults surface at the caller's next
- * synchronisation. The decode path allocates a grow-only workspace per device on first use
- * (FATTN_ERR_NOMEM if that fails); fattn_release() frees it.
+ * synchronisation. The decode path allocates a grow-only workspace per (device, stream) on first
+ * use (FATTN_ERR_NOMEM if that fails); fattn_release() frees it.
  */
 int attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
              int Hkv, int Tq, int Tk, int d, int causal, float scale, int dtype, void* stream);
@@ -238,8 +239,8 @@ const char* fattn_last_error(void);
 int fattn_version(void);
 
 /*
- * Free the workspaces (decode, backward) of every device after synchronising each device. Safe to call at
- * any time when no call of this library is in flight; later calls allocate again.
+ * Free the workspaces (split-K decode, backward) of every device after synchronising each device.
+ * Safe to call at any time when no call of this library is in flight; later calls allocate again.
  */
 int fattn_release(void);
 

@@ -1,4 +1,4 @@
-// Host side of libfattn: argument validation, launch planning, the decode workspace and the
+// Host side of libfattn: argument validation, launch planning, the workspaces and the
 // exported C entry points. Validation and planning make no HIP call, so every argument error is
 // reported identically on a machine without a GPU.
 #include <hip/hip_runtime.h>
@@ -151,8 +151,9 @@ int make_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dty
   return FATTN_OK;
 }
 
-// Grow-only decode workspace per (device, stream). The lock is held across the launches that
-// use it, so a buffer is never replaced while a call is between lookup and enqueue.
+// Grow-only workspace per (device, stream), shared by the split-K decode (partial outputs) and
+// the backward ((L, D) blocks). The lock is held across the launches that use it, so a buffer is
+// never replaced while a call is between lookup and enqueue.
 struct Workspace {
   float* ptr = nullptr;
   size_t floats = 0;
