@@ -18,7 +18,8 @@ work of the visible (query, key) pairs only, a packed batch of variable-length d
 a paged copy of its cache
 (attn_fwd_paged, 16-position pages in a random order; checked bitwise equal to the contiguous
 result), and the backward of the prefill call (attn_bwd, seeded upstream gradient), at
-10*B*H*T^2*d/2 FLOPs. One JSON line is printed.
+10*B*H*T^2*d/2 FLOPs. With the CPU baseline on, the fp64 oracle is also timed on bounded samples
+of those four calls (`cpu_oracle_beside`). One JSON line is printed.
 
     python bench.py --calibrate-copy BYTES
 
@@ -227,6 +228,76 @@ def cpu_baseline(budget_s=12.0, max_heads=32):
             "seconds": elapsed, "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def oracle_beside(budget_s=3.0):
+    """The fp64 oracle timed on bounded samples of the other measured calls (sliding window,
+    packed prefill, paged decode, backward), each in the unit of its GPU figure: heads (or
+    sequences) are added until `budget_s` seconds of oracle time have run."""
+    import numpy as np
+
+    import oracle
+    from tests import inputs
+
+    from threadpoolctl import threadpool_info
+
+    cfg = inputs.CONFIGS[PREFILL]
+    out = {"kind": "oracle",
+           "cores": max([i.get("num_threads", 1) for i in threadpool_info()] or [1])}
+
+    def heads_until(fn):
+        n, el = 0, 0.0
+        while n < cfg.Hq and (n == 0 or el < budget_s):
+            args = fn(n)
+            t0 = time.perf_counter()
+            args[0](*args[1:])
+            el += time.perf_counter() - t0
+            n += 1
+        return n, el
+
+    def head(h):
+        return (inputs.head_slice(cfg, inputs.Q_ID, 0, h), inputs.head_slice(cfg, inputs.K_ID, 0, h),
+                inputs.head_slice(cfg, inputs.V_ID, 0, h))
+
+    W = 4096
+    n, el = heads_until(lambda h: (lambda q, k, v: oracle.dense_head(q, k, v, True, cfg.scale,
+                                                                      window=W), *head(h)))
+    out["sliding_window_prefill"] = {
+        "value": 4.0 * cfg.d * n * window_pairs(cfg.Tq, W) / el / 1e12, "unit": "TFLOP/s",
+        "sample": f"{n} heads of the W=4096 T=8192 d=128 prefill, fp64 dense, {el:.2f} s"}
+
+    n, el = heads_until(lambda h: (lambda q, k, v, do: oracle.dense_backward_head(
+        q, k, v, do, True, cfg.scale), *head(h), inputs.grad_slice(cfg, 0, h)))
+    out["backward"] = {
+        "value": backward_flops(1, n, cfg.Tq, cfg.Tk, cfg.d, True) / el / 1e12, "unit": "TFLOP/s",
+        "sample": f"{n} heads of the causal T=8192 d=128 backward, fp64 chain rule with P "
+                  f"materialised, {el:.2f} s"}
+
+    lens = varlen_doc_lengths(VARLEN_TOKENS, 128, 8192, VARLEN_SEED)
+    vc = inputs.AttnConfig("varlen oracle sample", B=1, Hq=1, Hkv=1, Tq=1, Tk=1, d=cfg.d,
+                           dtype="bf16", causal=True, dist="normal", seed=VARLEN_SEED)
+    Q, K, V, cq, ck = inputs.make_packed(vc, lens[:2])
+    t0 = time.perf_counter()
+    oracle.varlen_attention(Q, K, V, cq, ck, True, cfg.scale)
+    el = time.perf_counter() - t0
+    out["varlen"] = {
+        "value": sum(prefill_flops(1, 1, m, m, cfg.d, True) for m in lens[:2]) / el / 1e12,
+        "unit": "TFLOP/s",
+        "sample": f"one head of the first two documents ({lens[0]} and {lens[1]} tokens) of the "
+                  f"packed batch, fp64 dense per document, {el:.2f} s"}
+
+    dc = inputs.CONFIGS[DECODE].replace(B=2, name="paged oracle sample")
+    Qd, _, _ = inputs.make_inputs(dc)
+    Kc, Vc, table, sl = inputs.make_paged(dc, 16, [dc.Tk] * dc.B)
+    t0 = time.perf_counter()
+    oracle.paged_decode(Qd[:, :, 0], Kc, Vc, table, sl, dc.scale)
+    el = time.perf_counter() - t0
+    out["paged_decode"] = {
+        "value": decode_bytes(dc.B, dc.Hq, dc.Hkv, dc.Tk, dc.d) / el / 1e9, "unit": "GB/s",
+        "sample": f"2 of the 64 sequences of the paged GQA decode (16-position pages), gather then "
+                  f"fp64 dense, {el:.2f} s"}
+    del np
+    return out
+
+
 def _r(d):
     return {k: round(v, 4) for k, v in d.items()}
 
@@ -400,9 +471,12 @@ def main():
     del do3, dq3, dk3, dv3
 
     cpu = None
+    beside = None
     if args.cpu_baseline == "auto":
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline()
+        print("[bench] timing the CPU oracle beside the other calls", file=sys.stderr, flush=True)
+        beside = oracle_beside()
 
     line = {
         "metric": METRIC,
@@ -483,6 +557,7 @@ def main():
             "traffic": traffic_for("backward_bf16.hip", "backward"),
         },
         "cpu_baseline": cpu,
+        "cpu_oracle_beside": beside,
     }
     print(json.dumps(line), flush=True)
 
