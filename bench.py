@@ -13,13 +13,13 @@ halved for the causal mask; the decode rate is reported as algorithmic HBM bytes
 
 After the timed steps, and outside them: the library's two probes (matrix-core rate on
 register operands, nontemporal HBM read rate) give the achievable rates the two kernels are also
-quoted against, the sliding-window variants of both calls (window 4096) are timed, with the
-work of the visible (query, key) pairs only, a packed batch of variable-length documents (attn_fwd_varlen, 32768 tokens), the decode call over
-a paged copy of its cache
-(attn_fwd_paged, 16-position pages in a random order; checked bitwise equal to the contiguous
-result), and the backward of the prefill call (attn_bwd, seeded upstream gradient), at
-10*B*H*T^2*d/2 FLOPs. With the CPU baseline on, the fp64 oracle is also timed on bounded samples
-of those four calls (`cpu_oracle_beside`). One JSON line is printed.
+quoted against; then the sliding-window variants of both calls (window 4096, work of the visible
+(query, key) pairs only), a packed batch of variable-length documents (attn_fwd_varlen and
+attn_bwd_varlen, 32768 tokens), the decode call over a paged copy of its cache (attn_fwd_paged,
+16-position pages in a random order, checked bitwise equal to the contiguous result) and the
+backward of the prefill call (attn_bwd, seeded upstream gradient, 10*B*H*T^2*d/2 FLOPs) are timed.
+With the CPU baseline on, the fp64 oracle is also timed on bounded samples of those calls
+(`cpu_oracle_beside`). One JSON line is printed.
 
     python bench.py --calibrate-copy BYTES
 
@@ -453,7 +453,18 @@ def main():
         sys.exit(1)
     vl_flops = sum(prefill_flops(1, pc.Hq, n, n, pc.d, True) for n in lens)
     vl_tflops = vl_flops / (vl["median"] * 1e-3) / 1e12
-    del qv, kv, vv, ov, lv
+    # and its backward (attn_bwd_varlen) with a seeded upstream gradient
+    dov = torch.randn(VARLEN_TOKENS, pc.Hq, pc.d, device="cuda", generator=gv).to(torch.bfloat16)
+    gq, gk, gvv = torch.empty_like(qv), torch.empty_like(kv), torch.empty_like(vv)
+    vb = stats_ms(time_calls(torch, lambda: fa.attn_bwd_varlen(
+        qv, kv, vv, ov, lv, dov, cu, cu, max(lens), max(lens), causal=True, scale=pc.scale,
+        dq=gq, dk=gk, dv=gvv), 5, 10))
+    if not all(bool(torch.isfinite(t).all()) for t in (gq, gk, gvv)):
+        print("non-finite packed gradient", file=sys.stderr)
+        sys.exit(1)
+    vb_flops = 2.5 * vl_flops
+    vb_tflops = vb_flops / (vb["median"] * 1e-3) / 1e12
+    del qv, kv, vv, ov, lv, dov, gq, gk, gvv
 
     # ---- the backward of the prefill call (O and LSE of the last forward call above)
     print("[bench] backward", file=sys.stderr, flush=True)
@@ -536,6 +547,10 @@ def main():
             "flops_per_call": vl_flops, "ms_stats": _r(vl),
             "work": "sum over documents of 4*H*L^2*d/2 (the causal count of each document)",
             "traffic": traffic_for("prefill_bf16.hip", "prefill_varlen"),
+            "backward": {"ms": round(vb["median"], 4), "tflops": round(vb_tflops, 2),
+                         "pct_mfma_peak": round(100 * vb_tflops / PEAK_BF16_TFLOPS, 2),
+                         "flops_per_call": vb_flops, "ms_stats": _r(vb),
+                         "work": "2.5 times the forward count: the five backward products"},
         },
         "paged_decode": {
             "workload": "GQA decode bf16 B=64 Hq=64 Hkv=8 Tk=8192 d=128 over a paged cache, "

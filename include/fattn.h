@@ -225,6 +225,26 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
              const float* LSE, void* dQ, void* dK, void* dV, int B, int Hq, int Hkv, int Tq,
              int Tk, int d, int causal, int window, float scale, int dtype, void* stream);
 
+/*
+ * attn_bwd_varlen: attn_bwd over a packed batch, the backward of attn_fwd_varlen: each sequence's
+ * gradients are those of attn_bwd on its slices (no gradient flows between sequences).
+ *
+ *   Q, O, dO, dQ  [total_q, Hq, d]  bf16 (dQ written)
+ *   K, V, dK, dV  [total_k, Hkv, d] bf16 (dK, dV written)
+ *   LSE           [Hq, total_q]     float32, as written by attn_fwd_varlen
+ *   cu_seqlens_q, cu_seqlens_k, num_seqs, total_q, total_k, max_seqlen_q, max_seqlen_k, causal,
+ *   window: as for attn_fwd_varlen.
+ *
+ * Rows that see no key contribute nothing and get dQ = 0; keys no row sees get dK = dV = 0.
+ * Errors: those of attn_fwd_varlen and attn_bwd, plus FATTN_ERR_INVALID when Hq * total_q
+ * exceeds 2^28 - 1. Uses the per-(device, stream) workspace (2 * Hq * total_q floats).
+ */
+int attn_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* LSE, void* dQ, void* dK, void* dV, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int num_seqs, int total_q, int total_k,
+                    int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d, int causal,
+                    int window, float scale, int dtype, void* stream);
+
 /* Text for a return code (static storage). */
 const char* fattn_strerror(int code);
 

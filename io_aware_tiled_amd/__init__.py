@@ -76,6 +76,8 @@ lib.attn_fwd_window.restype = _i
 lib.attn_fwd_window_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
 lib.attn_fwd_window_cfg.restype = _i
 lib.attn_fwd_varlen.argtypes = [_vp] * 7 + [_i] * 10 + [_f, _i, _vp]
+lib.attn_bwd_varlen.argtypes = [_vp] * 11 + [_i] * 10 + [_f, _i, _vp]
+lib.attn_bwd_varlen.restype = _i
 lib.attn_fwd_varlen.restype = _i
 lib.attn_fwd_paged.argtypes = [_vp] * 7 + [_i] * 7 + [_f, _i, _vp]
 lib.attn_fwd_paged.restype = _i
@@ -385,3 +387,70 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     if rc != FATTN_OK:
         raise FattnError(rc, fattn_last_error())
     return out, lse
+
+
+def attn_bwd_varlen_raw(Q, K, V, O, dO, LSE, dQ, dK, dV, cu_q, cu_k, num_seqs, total_q, total_k,
+                        max_q, max_k, Hq, Hkv, d, causal, window, scale, dtype, stream) -> int:
+    """The C call attn_bwd_varlen with plain integers for pointers; returns the status code."""
+    return lib.attn_bwd_varlen(Q, K, V, O, dO, LSE, dQ, dK, dV, cu_q, cu_k, num_seqs, total_q,
+                               total_k, max_q, max_k, Hq, Hkv, d, causal, window, scale, dtype,
+                               stream)
+
+
+def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                    max_seqlen_k: int, causal: bool = False, scale: Optional[float] = None,
+                    window: Optional[int] = None, dq=None, dk=None, dv=None, stream=None):
+    """Backward of attn_fwd_varlen; returns (dq, dk, dv) in the packed layouts.
+
+    q, o, do: [total_q, Hq, d]; k, v: [total_k, Hkv, d]; bfloat16; lse: float32 [Hq, total_q]
+    from the forward call with the same offsets, causal, window and scale.
+    """
+    import torch
+
+    if window is not None and not causal:
+        raise ValueError("a sliding window is a causal mask: pass causal=True")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [total, H, d]")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise TypeError(f"{name} must be a 1-D int32 tensor")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("lse", lse),
+                    ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk_ = k.shape
+    if dk_ != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [total_k, Hkv, d] with q's d")
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("o and do must have q's shape")
+    if tuple(lse.shape) != (Hq, total_q):
+        raise ValueError("lse must be [Hq, total_q]")
+    num_seqs = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != num_seqs + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = attn_bwd_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                             max(num_seqs, 0), total_q, total_k, int(max_seqlen_q),
+                             int(max_seqlen_k), Hq, Hkv, d, int(bool(causal)), int(window or 0),
+                             float(scale), FATTN_BF16, stream)
+    if rc != FATTN_OK:
+        raise FattnError(rc, fattn_last_error())
+    return dq, dk, dv

@@ -370,6 +370,76 @@ extern "C" int attn_fwd_varlen(const void* Q, const void* K, const void* V, void
   return e == hipSuccess ? FATTN_OK : hip_fail(FATTN_ERR_HIP, "kernel launch", e);
 }
 
+extern "C" int attn_bwd_varlen(const void* Q, const void* K, const void* V, const void* O,
+                               const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                               const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                               int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                               int Hq, int Hkv, int d, int causal, int window, float scale,
+                               int dtype, void* stream) {
+  g_last_error[0] = 0;
+  if (num_seqs < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(FATTN_ERR_INVALID, "negative size");
+  if (window < 0) return fail(FATTN_ERR_INVALID, "window must be >= 0");
+  if (window > 0 && causal != 1) return fail(FATTN_ERR_INVALID, "a window needs causal = 1");
+  const int tk_check = max_seqlen_k > max_seqlen_q ? max_seqlen_k : max_seqlen_q;
+  bool noop;
+  int rc = validate_shape(num_seqs, Hq, Hkv, max_seqlen_q, tk_check > 0 ? tk_check : 1, d,
+                          causal, dtype, &noop);
+  if (rc != FATTN_OK) return rc;
+  if (!std::isfinite(scale)) return fail(FATTN_ERR_INVALID, "scale is not finite");
+  if (noop || total_q == 0) return FATTN_OK;
+  if (dtype != FATTN_BF16) return fail(FATTN_ERR_UNSUPPORTED, "backward is bf16 only");
+  if ((long long)Hq * total_q * 8 > 0x7fffffffLL)
+    return fail(FATTN_ERR_INVALID, "Hq * total_q too large for the packed backward");
+  if ((long long)Hq * d * 2 * 64 > 0x7fffffffLL || (long long)Hkv * d * 2 * 64 > 0x7fffffffLL)
+    return fail(FATTN_ERR_INVALID, "H * d too large");
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV || !cu_seqlens_q ||
+      !cu_seqlens_k)
+    return fail(FATTN_ERR_INVALID, "NULL pointer");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+    return fail(FATTN_ERR_INVALID, "tensor pointer not 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return fail(FATTN_ERR_INVALID, "cu_seqlens not 4-byte aligned");
+  if (window >= max_seqlen_k) window = 0;
+
+  BwdProblem p;
+  p.Q = Q;
+  p.K = K;
+  p.V = V;
+  p.O = O;
+  p.dO = dO;
+  p.LSE = LSE;
+  p.dQ = dQ;
+  p.dK = dK;
+  p.dV = dV;
+  p.B = num_seqs;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Tq = max_seqlen_q;
+  p.Tk = max_seqlen_k;
+  p.d = d;
+  p.causal = causal;
+  p.window = window;
+  p.scale = scale;
+  Packed pk;
+  pk.cu_q = cu_seqlens_q;
+  pk.cu_k = cu_seqlens_k;
+  pk.total_q = total_q;
+  pk.total_k = total_k;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipGetDevice", he);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  float* ws = nullptr;
+  rc = workspace(dev, s, (size_t)2 * Hq * total_q, &ws);
+  if (rc != FATTN_OK) return rc;
+  he = launch_backward_varlen_bf16(p, pk, ws, s);
+  return he == hipSuccess ? FATTN_OK : hip_fail(FATTN_ERR_HIP, "kernel launch", he);
+}
+
 extern "C" int attn_fwd_paged(const void* Q, const void* K_cache, const void* V_cache,
                               const int* block_table, const int* seq_lens, void* O, float* LSE,
                               int B, int Hq, int Hkv, int d, int num_blocks, int block_size,

@@ -43,6 +43,39 @@ constexpr float kPosInf = __builtin_inff();
 
 // ---- D_i = sum_d dO[i, d] * O[i, d] and L_i * log2(e), per 32-row block of every head.
 // D / 8 lanes read a row (16 bytes each) and reduce across themselves.
+// Packed batches: one row per (query head, token) of [total_q, Hq, D] tensors; L and D are
+// written to ws[h * total_q + token] and ws[Hq * total_q + h * total_q + token] (no padding rows:
+// the gradient kernels mask rows outside a sequence).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_packed_kernel(const __bf16* __restrict__ O,
+                                                              const __bf16* __restrict__ dO,
+                                                              const float* __restrict__ LSE,
+                                                              float* __restrict__ ws, int Hq,
+                                                              int total_q) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int sub = tid % LPR;
+  const long long r = (long long)blockIdx.x * RPB + tid / LPR;  // over Hq * total_q rows
+  const bool valid = r < (long long)Hq * total_q;
+  const int h = valid ? (int)(r / total_q) : 0;
+  const int g = valid ? (int)(r - (long long)h * total_q) : 0;
+  float acc = 0.f;
+  if (valid) {
+    const size_t e = ((size_t)g * Hq + h) * D + 8 * sub;
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + e);
+    const bf16x8 gr = *reinterpret_cast<const bf16x8*>(dO + e);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc = fmaf((float)o[k], (float)gr[k], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (sub == 0 && valid) {
+    ws[r] = LSE[r] * kLog2eF;
+    ws[(size_t)Hq * total_q + r] = acc;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ O,
                                                        const __bf16* __restrict__ dO,
@@ -85,11 +118,15 @@ __device__ __forceinline__ int xcd_order(int lin, int total) {
 }
 
 // ---- dQ: one workgroup per (batch, query head, block of 32 * NW query rows).
-template <int D, int BC, int NW>
+// VARLEN: packed batch (Q, dO, dQ [total_q, Hq, D], K, V [total_k, Hkv, D], the workspace of
+// bwd_prep_packed_kernel); blockIdx covers (sequence, head, query block) with Tq and Tk the
+// longest lengths, and each workgroup takes its sequence's lengths from the offsets.
+template <int D, int BC, int NW, bool VARLEN>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dQ, int Hq,
-    int Hkv, int Tq, int Tk, int causal, int window, float scale, float c) {
+    int Hkv, int Tq, int Tk, int causal, int window, float scale, float c,
+    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
   using S = Shape<D, BC, NW>;
   __shared__ __align__(1024) unsigned char k_st0[S::TILE], k_st1[S::TILE];
   __shared__ __align__(1024) unsigned char v_st0[S::TILE], v_st1[S::TILE];
@@ -108,13 +145,27 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int g = h / (Hq / Hkv);
+  int q_begin = 0, k_begin = 0;
+  if constexpr (VARLEN) {
+    q_begin = min(max(cu_q[b], 0), total_q);
+    const int q_stop = min(max(cu_q[b + 1], q_begin), total_q);
+    k_begin = min(max(cu_k[b], 0), total_k);
+    const int k_stop = min(max(cu_k[b + 1], k_begin), total_k);
+    Tq = min(q_stop - q_begin, Tq);
+    Tk = min(k_stop - k_begin, Tk);
+    if (qb * S::BR >= Tq) return;  // the whole workgroup: past this sequence's rows
+  }
   const int off = Tk - Tq;
   const int nqt = (Tq + 31) / 32;
+  const size_t qstr = VARLEN ? (size_t)Hq * D : (size_t)D;   // elements between rows
+  const size_t kstr = VARLEN ? (size_t)Hkv * D : (size_t)D;
 
-  const __bf16* Qh = Q + (size_t)bh * Tq * D;
-  const __bf16* dOh = dO + (size_t)bh * Tq * D;
-  const __bf16* Kh = K + ((size_t)b * Hkv + g) * (size_t)Tk * D;
-  const __bf16* Vh = V + ((size_t)b * Hkv + g) * (size_t)Tk * D;
+  const __bf16* Qh = VARLEN ? Q + ((size_t)q_begin * Hq + h) * D : Q + (size_t)bh * Tq * D;
+  const __bf16* dOh = VARLEN ? dO + ((size_t)q_begin * Hq + h) * D : dO + (size_t)bh * Tq * D;
+  const __bf16* Kh = VARLEN ? K + ((size_t)k_begin * Hkv + g) * D
+                            : K + ((size_t)b * Hkv + g) * (size_t)Tk * D;
+  const __bf16* Vh = VARLEN ? V + ((size_t)k_begin * Hkv + g) * D
+                            : V + ((size_t)b * Hkv + g) * (size_t)Tk * D;
 
   // key tiles: the same ranges as the forward pass of this query block
   const int i0 = qb * S::BR;
@@ -139,26 +190,39 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   for (int kk = 0; kk < D / 16; ++kk) {
     u32x4 rq = {0u, 0u, 0u, 0u}, ro = {0u, 0u, 0u, 0u};
     if (qrow < Tq) {
-      rq = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + 16 * kk + 8 * hf);
-      ro = *reinterpret_cast<const u32x4*>(dOh + (size_t)qrow * D + 16 * kk + 8 * hf);
+      rq = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * qstr + 16 * kk + 8 * hf);
+      ro = *reinterpret_cast<const u32x4*>(dOh + (size_t)qrow * qstr + 16 * kk + 8 * hf);
     }
     qb8[kk] = __builtin_bit_cast(bf16x8, rq);
     ob8[kk] = __builtin_bit_cast(bf16x8, ro);
   }
   float Lr = kPosInf, Dr = 0.f;
   if (qrow < Tq) {
-    const float* blk = ws + ((size_t)bh * nqt + qrow / 32) * 64;
-    Lr = blk[qrow % 32];
-    Dr = blk[32 + qrow % 32];
+    if constexpr (VARLEN) {
+      const size_t r = (size_t)h * total_q + q_begin + qrow;
+      Lr = ws[r];
+      Dr = ws[(size_t)Hq * total_q + r];
+    } else {
+      const float* blk = ws + ((size_t)bh * nqt + qrow / 32) * 64;
+      Lr = blk[qrow % 32];
+      Dr = blk[32 + qrow % 32];
+    }
   }
 
+  const int krb = VARLEN ? (int)(kstr * 2) : S::RB;  // bytes between K (V) rows in memory
   int dvo[S::NI_W];
 #pragma unroll
   for (int i = 0; i < S::NI_W; ++i) {
     const int q = wave + i * NW;
     const int r = q * S::RPI + lane / S::C;
-    dvo[i] = r * S::RB + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
+    dvo[i] = r * krb + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
   }
+  auto load_tile = [&](const __bf16* head, int j0, unsigned char* dst) {
+    if constexpr (VARLEN)
+      dma_tile_strided<D, BC, NW>(head, j0, Tk, (int)kstr, dst, wave, dvo);
+    else
+      dma_tile<D, BC, NW>(head, j0, Tk, dst, wave, dvo);
+  };
   const int ka = rowbase<D, BC, NW>(col) ^ (hf << 4);
   const int vq = lane >> 5, vg = (lane >> 4) & 1, ve = (lane >> 2) & 3, va = lane & 3;
   int vab[2];
@@ -245,8 +309,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   }
   __syncthreads();
   if (j_lo < ntiles) {
-    dma_tile<D, BC, NW>(Kh, j_lo * BC, Tk, k_st0, wave, dvo);
-    dma_tile<D, BC, NW>(Vh, j_lo * BC, Tk, v_st0, wave, dvo);
+    load_tile(Kh, j_lo * BC, k_st0);
+    load_tile(Vh, j_lo * BC, v_st0);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -254,8 +318,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   auto step = [&](int j, const unsigned char* k_cur, const unsigned char* v_cur,
                   unsigned char* k_nxt, unsigned char* v_nxt) {
     if (j + 1 < ntiles) {
-      dma_tile<D, BC, NW>(Kh, (j + 1) * BC, Tk, k_nxt, wave, dvo);
-      dma_tile<D, BC, NW>(Vh, (j + 1) * BC, Tk, v_nxt, wave, dvo);
+      load_tile(Kh, (j + 1) * BC, k_nxt);
+      load_tile(Vh, (j + 1) * BC, v_nxt);
     }
     if (active(j)) compute(j, k_cur, v_cur);
     __builtin_amdgcn_s_waitcnt(0);
@@ -269,7 +333,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   if (j < ntiles) step(j, k_st0, v_st0, k_st1, v_st1);
 
   if (qrow >= Tq) return;
-  __bf16* row = dQ + ((size_t)bh * Tq + qrow) * D;
+  __bf16* row = VARLEN ? dQ + ((size_t)(q_begin + qrow) * Hq + h) * D
+                       : dQ + ((size_t)bh * Tq + qrow) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -284,12 +349,14 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
 // ---- dK, dV: one workgroup per (batch, kv head, block of 32 * NW keys); the loop runs over the
 // query heads of the group and, in each, over the query tiles of BC rows that see a key of the
 // block.
-template <int D, int BC, int NW, int MINW>
+// VARLEN: packed batch, as for the dQ kernel; blockIdx covers (sequence, kv head, key block).
+template <int D, int BC, int NW, int MINW, bool VARLEN>
 __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dK,
     __bf16* __restrict__ dV, int Hq, int Hkv, int Tq, int Tk, int causal, int window, float scale,
-    float c) {
+    float c, const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q,
+    int total_k) {
   using S = Shape<D, BC, NW>;
   constexpr int BK = 32 * NW;     // keys per workgroup
   constexpr int LWB = BC / 32;    // (L, D) blocks per query tile
@@ -311,15 +378,27 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
   const int G = Hq / Hkv;
+  const int k0 = kb * BK;
+  int q_begin = 0, k_begin = 0;
+  if constexpr (VARLEN) {
+    q_begin = min(max(cu_q[b], 0), total_q);
+    const int q_stop = min(max(cu_q[b + 1], q_begin), total_q);
+    k_begin = min(max(cu_k[b], 0), total_k);
+    const int k_stop = min(max(cu_k[b + 1], k_begin), total_k);
+    Tq = min(q_stop - q_begin, Tq);
+    Tk = min(k_stop - k_begin, Tk);
+    if (k0 >= Tk) return;  // the whole workgroup: past this sequence's keys
+  }
   const int off = Tk - Tq;
   const int nqt = (Tq + 31) / 32;
+  const size_t qstr = VARLEN ? (size_t)Hq * D : (size_t)D;   // elements between rows
+  const size_t kstr = VARLEN ? (size_t)Hkv * D : (size_t)D;
 
-  const int k0 = kb * BK;
   const int kw0 = k0 + 32 * wave;
   const int kcol = kw0 + col;
   const int k_last = min(Tk - 1, k0 + BK - 1);
-  const __bf16* Kh = K + (size_t)bg * Tk * D;
-  const __bf16* Vh = V + (size_t)bg * Tk * D;
+  const __bf16* Kh = VARLEN ? K + ((size_t)k_begin * Hkv + g) * D : K + (size_t)bg * Tk * D;
+  const __bf16* Vh = VARLEN ? V + ((size_t)k_begin * Hkv + g) * D : V + (size_t)bg * Tk * D;
 
   // ---- this lane's key: K^T and V^T operands
   bf16x8 kb8[D / 16], vb8[D / 16];
@@ -327,8 +406,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   for (int kk = 0; kk < D / 16; ++kk) {
     u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
     if (kcol < Tk) {
-      rk = *reinterpret_cast<const u32x4*>(Kh + (size_t)kcol * D + 16 * kk + 8 * hf);
-      rv = *reinterpret_cast<const u32x4*>(Vh + (size_t)kcol * D + 16 * kk + 8 * hf);
+      rk = *reinterpret_cast<const u32x4*>(Kh + (size_t)kcol * kstr + 16 * kk + 8 * hf);
+      rv = *reinterpret_cast<const u32x4*>(Vh + (size_t)kcol * kstr + 16 * kk + 8 * hf);
     }
     kb8[kk] = __builtin_bit_cast(bf16x8, rk);
     vb8[kk] = __builtin_bit_cast(bf16x8, rv);
@@ -342,12 +421,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   const int ntq = i_lo <= i_hi ? i_hi / BC - t_lo + 1 : 0;
   const int nsteps = G * ntq;
 
+  const int qrb = VARLEN ? (int)(qstr * 2) : S::RB;  // bytes between Q (dO) rows in memory
   int dvo[S::NI_W];
 #pragma unroll
   for (int i = 0; i < S::NI_W; ++i) {
     const int q = wave + i * NW;
     const int r = q * S::RPI + lane / S::C;
-    dvo[i] = r * S::RB + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
+    dvo[i] = r * qrb + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
   }
   const int ka = rowbase<D, BC, NW>(col) ^ (hf << 4);
   const int vq = lane >> 5, vg = (lane >> 4) & 1, ve = (lane >> 2) & 3, va = lane & 3;
@@ -360,14 +440,32 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   auto issue = [&](int s, unsigned char* qst, unsigned char* ost, float* lw) {
     const int hh = g * G + s / ntq;
     const int q0 = (t_lo + s % ntq) * BC;
-    const size_t bh = (size_t)b * Hq + hh;
-    dma_tile<D, BC, NW>(Q + bh * Tq * D, q0, Tq, qst, wave, dvo);
-    dma_tile<D, BC, NW>(dO + bh * Tq * D, q0, Tq, ost, wave, dvo);
-    if (wave < LWB) {
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(ws + bh * nqt * 64), (short)0, nqt * 256, kBufferFlags);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lw + 64 * wave), 4,
-                                               (q0 / 32 + wave) * 256 + 4 * lane, 0, 0, 0);
+    if constexpr (VARLEN) {
+      const size_t head = (size_t)q_begin * Hq + hh;
+      dma_tile_strided<D, BC, NW>(Q + head * D, q0, Tq, (int)qstr, qst, wave, dvo);
+      dma_tile_strided<D, BC, NW>(dO + head * D, q0, Tq, (int)qstr, ost, wave, dvo);
+      if (wave < LWB) {
+        // lanes 0-31: L of rows q0 + 32*wave + lane, lanes 32-63: D of the same rows; rows past
+        // the sequence are masked, rows past the batch read as zeros
+        const size_t plane = (size_t)Hq * total_q;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(ws), (short)0, (int)min(plane * 8, (size_t)0x7fffffff),
+            kBufferFlags);
+        const size_t r = (size_t)hh * total_q + q_begin + q0 + 32 * wave + (lane & 31);
+        const size_t at = (lane < 32 ? r : plane + r) * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lw + 64 * wave), 4,
+                                                 (int)at, 0, 0, 0);
+      }
+    } else {
+      const size_t bh = (size_t)b * Hq + hh;
+      dma_tile<D, BC, NW>(Q + bh * Tq * D, q0, Tq, qst, wave, dvo);
+      dma_tile<D, BC, NW>(dO + bh * Tq * D, q0, Tq, ost, wave, dvo);
+      if (wave < LWB) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(ws + bh * nqt * 64), (short)0, nqt * 256, kBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(lw + 64 * wave), 4,
+                                                 (q0 / 32 + wave) * 256 + 4 * lane, 0, 0, 0);
+      }
     }
   };
 
@@ -486,8 +584,10 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   if (s < nsteps) step(s, q_st0, o_st0, lw_st0, q_st1, o_st1, lw_st1);
 
   if (kcol >= Tk) return;
-  __bf16* krow = dK + ((size_t)bg * Tk + kcol) * D;
-  __bf16* vrow = dV + ((size_t)bg * Tk + kcol) * D;
+  __bf16* krow = VARLEN ? dK + ((size_t)(k_begin + kcol) * Hkv + g) * D
+                        : dK + ((size_t)bg * Tk + kcol) * D;
+  __bf16* vrow = VARLEN ? dV + ((size_t)(k_begin + kcol) * Hkv + g) * D
+                        : dV + ((size_t)bg * Tk + kcol) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -503,7 +603,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
 }
 
 template <int D>
-hipError_t launch_d(const BwdProblem& p, float* ws, hipStream_t stream) {
+hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_t stream) {
   const int BH = p.B * p.Hq;
   const int nqt = (p.Tq + 31) / 32;
   const float c = p.scale * kLog2eF;
@@ -511,36 +611,66 @@ hipError_t launch_d(const BwdProblem& p, float* ws, hipStream_t stream) {
   const __bf16* K = static_cast<const __bf16*>(p.K);
   const __bf16* V = static_cast<const __bf16*>(p.V);
   const __bf16* dO = static_cast<const __bf16*>(p.dO);
+  const int* cu_q = pk ? pk->cu_q : nullptr;
+  const int* cu_k = pk ? pk->cu_k : nullptr;
+  const int total_q = pk ? pk->total_q : 0, total_k = pk ? pk->total_k : 0;
 
   constexpr int RPB = 256 / (D / 8);
-  const long long rows = (long long)BH * nqt * 32;
-  bwd_prep_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(
-      static_cast<const __bf16*>(p.O), dO, p.LSE, ws, BH, p.Tq, nqt);
+  if (pk) {
+    const long long rows = (long long)p.Hq * total_q;
+    bwd_prep_packed_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                                stream>>>(static_cast<const __bf16*>(p.O), dO, p.LSE, ws, p.Hq,
+                                          total_q);
+  } else {
+    const long long rows = (long long)BH * nqt * 32;
+    bwd_prep_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(
+        static_cast<const __bf16*>(p.O), dO, p.LSE, ws, BH, p.Tq, nqt);
+  }
 
   constexpr int DQ_NW = 8, DQ_BC = 32;
   const int nqb = (p.Tq + 32 * DQ_NW - 1) / (32 * DQ_NW);
-  bwd_dq_kernel<D, DQ_BC, DQ_NW><<<dim3((unsigned)(BH * nqb)), dim3(64 * DQ_NW), 0, stream>>>(
-      Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal, p.window,
-      p.scale, c);
+  const dim3 dq_grid((unsigned)(BH * nqb)), dq_block(64 * DQ_NW);
+  if (pk)
+    bwd_dq_kernel<D, DQ_BC, DQ_NW, true><<<dq_grid, dq_block, 0, stream>>>(
+        Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
+        p.window, p.scale, c, cu_q, cu_k, total_q, total_k);
+  else
+    bwd_dq_kernel<D, DQ_BC, DQ_NW, false><<<dq_grid, dq_block, 0, stream>>>(
+        Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
+        p.window, p.scale, c, nullptr, nullptr, 0, 0);
 
   constexpr int KV_NW = 4, KV_BC = 32, KV_MINW = D >= 128 ? 1 : 2;
   const int nkb = (p.Tk + 32 * KV_NW - 1) / (32 * KV_NW);
-  bwd_dkdv_kernel<D, KV_BC, KV_NW, KV_MINW>
-      <<<dim3((unsigned)(p.B * p.Hkv * nkb)), dim3(64 * KV_NW), 0, stream>>>(
-          Q, K, V, dO, ws, static_cast<__bf16*>(p.dK), static_cast<__bf16*>(p.dV), p.Hq, p.Hkv,
-          p.Tq, p.Tk, p.causal, p.window, p.scale, c);
+  const dim3 kv_grid((unsigned)(p.B * p.Hkv * nkb)), kv_block(64 * KV_NW);
+  if (pk)
+    bwd_dkdv_kernel<D, KV_BC, KV_NW, KV_MINW, true><<<kv_grid, kv_block, 0, stream>>>(
+        Q, K, V, dO, ws, static_cast<__bf16*>(p.dK), static_cast<__bf16*>(p.dV), p.Hq, p.Hkv,
+        p.Tq, p.Tk, p.causal, p.window, p.scale, c, cu_q, cu_k, total_q, total_k);
+  else
+    bwd_dkdv_kernel<D, KV_BC, KV_NW, KV_MINW, false><<<kv_grid, kv_block, 0, stream>>>(
+        Q, K, V, dO, ws, static_cast<__bf16*>(p.dK), static_cast<__bf16*>(p.dV), p.Hq, p.Hkv,
+        p.Tq, p.Tk, p.causal, p.window, p.scale, c, nullptr, nullptr, 0, 0);
   return hipGetLastError();
+}
+
+hipError_t launch_any(const BwdProblem& p, const Packed* pk, float* ws, hipStream_t stream) {
+  switch (p.d) {
+    case 32: return launch_d<32>(p, pk, ws, stream);
+    case 64: return launch_d<64>(p, pk, ws, stream);
+    case 128: return launch_d<128>(p, pk, ws, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_backward_bf16(const BwdProblem& p, float* ws, hipStream_t stream) {
-  switch (p.d) {
-    case 32: return launch_d<32>(p, ws, stream);
-    case 64: return launch_d<64>(p, ws, stream);
-    case 128: return launch_d<128>(p, ws, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_any(p, nullptr, ws, stream);
+}
+
+hipError_t launch_backward_varlen_bf16(const BwdProblem& p, const Packed& pk, float* ws,
+                                       hipStream_t stream) {
+  return launch_any(p, &pk, ws, stream);
 }
 
 }  // namespace fattn

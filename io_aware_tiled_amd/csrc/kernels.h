@@ -98,4 +98,10 @@ inline size_t backward_workspace_floats(int B, int Hq, int Tq) {
 // ws holds backward_workspace_floats(B, Hq, Tq) floats. d in {32, 64, 128}.
 hipError_t launch_backward_bf16(const BwdProblem& p, float* ws, hipStream_t stream);
 
+// The same over a packed batch: p.B is the number of sequences, p.Tq and p.Tk the longest
+// lengths; Q, O, dO, dQ are [total_q, Hq, d], K, V, dK, dV [total_k, Hkv, d], LSE [Hq, total_q];
+// ws holds 2 * Hq * total_q floats.
+hipError_t launch_backward_varlen_bf16(const BwdProblem& p, const Packed& pk, float* ws,
+                                       hipStream_t stream);
+
 }  // namespace fattn

@@ -41,5 +41,5 @@ from .backward import (  # noqa: F401
     tiled_backward_head,
 )
 from .paged import gather_sequence, paged_decode  # noqa: F401
-from .varlen import varlen_attention  # noqa: F401
+from .varlen import varlen_attention, varlen_backward  # noqa: F401
 from . import accounting  # noqa: F401

@@ -21,6 +21,7 @@ from typing import Optional
 import numpy as np
 
 from .attention import _kv_head, dense_head
+from .backward import tiled_backward_head
 
 
 def varlen_attention(Q, K, V, cu_q, cu_k, causal: bool, scale: Optional[float] = None,
@@ -53,4 +54,39 @@ def varlen_attention(Q, K, V, cu_q, cu_k, causal: bool, scale: Optional[float] =
     return O, L
 
 
-__all__ = ["varlen_attention"]
+def varlen_backward(Q, K, V, O, LSE, dO, cu_q, cu_k, causal: bool, scale: Optional[float] = None,
+                    window: Optional[int] = None):
+    """Gradients of ``varlen_attention``: each document through ``tiled_backward_head`` (the
+    pages' backward from O and L) on its slices; a kv head's dK, dV add over its query heads.
+
+    O, dO: [total_q, Hq, d]; LSE: [Hq, total_q]. Rows that see no key are left out of their
+    document's problem (their dQ is 0 and they add nothing to dK, dV).
+    Returns (dQ [total_q, Hq, d], dK [total_k, Hkv, d], dV [total_k, Hkv, d]).
+    """
+    Q, K, V, O, LSE, dO = (np.asarray(x) for x in (Q, K, V, O, LSE, dO))
+    total_q, Hq, d = Q.shape
+    total_k, Hkv = K.shape[0], K.shape[1]
+    dQ = np.zeros((total_q, Hq, d))
+    dK = np.zeros((total_k, Hkv, d))
+    dV = np.zeros((total_k, Hkv, d))
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        tq, tk = q1 - q0, k1 - k0
+        if tq <= 0 or tk <= 0:
+            continue
+        first = max(0, tq - tk) if causal else 0
+        r0 = q0 + first
+        if r0 >= q1:
+            continue
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            gq, gk, gv = tiled_backward_head(Q[r0:q1, h], K[k0:k1, g], V[k0:k1, g], O[r0:q1, h],
+                                             LSE[h, r0:q1], dO[r0:q1, h], causal, scale,
+                                             window=window)
+            dQ[r0:q1, h] = gq
+            dK[k0:k1, g] += gk
+            dV[k0:k1, g] += gv
+    return dQ, dK, dV
+
+
+__all__ = ["varlen_attention", "varlen_backward"]

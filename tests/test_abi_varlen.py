@@ -61,3 +61,35 @@ def test_python_binding_checks():
         fa.attn_fwd_varlen(q, q, q, cu.long(), cu, 10, 10)
     with pytest.raises(ValueError):
         fa.attn_fwd_varlen(q, q, q, cu, cu, 10, 10, causal=False, window=3)
+
+
+BPTRS = ("Q", "K", "V", "O", "dO", "LSE", "dQ", "dK", "dV", "cu_q", "cu_k")
+
+
+def _bcall(**kw):
+    a = dict(n=3, total_q=300, total_k=300, max_q=200, max_k=200, Hq=8, Hkv=2, d=64, causal=1,
+             window=0, scale=0.125, dtype=BF16, stream=None)
+    a.update({n: P for n in BPTRS})
+    a.update(kw)
+    return fa.attn_bwd_varlen_raw(*(a[n] for n in BPTRS), a["n"], a["total_q"], a["total_k"],
+                                  a["max_q"], a["max_k"], a["Hq"], a["Hkv"], a["d"], a["causal"],
+                                  a["window"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [{n: None} for n in BPTRS] + [
+    dict(dQ=P + 2), dict(dK=P + 8), dict(LSE=P + 4), dict(cu_k=P + 2),
+    dict(n=-1), dict(total_q=-1), dict(Hkv=3), dict(causal=2), dict(window=-1),
+    dict(window=4, causal=0), dict(scale=float("nan")), dict(total_q=1 << 26, Hq=8),
+])
+def test_backward_invalid_arguments(kw):
+    assert _bcall(**kw) == INVALID, fa.fattn_last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(dtype=F32)])
+def test_backward_unsupported(kw):
+    assert _bcall(**kw) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(n=0), dict(total_q=0), dict(n=0, **{n: None for n in BPTRS})])
+def test_backward_empty_problems_are_noops(kw):
+    assert _bcall(**kw) == OK

@@ -82,3 +82,56 @@ def test_rows_without_keys_and_window():
     Q, K, V, cq, ck = inputs.make_packed(cfg, [5, 7])
     O, _ = oracle.varlen_attention(Q, K, V, cq, ck, True, window=1)
     assert np.array_equal(O[:, 0], V[:, 0].astype(np.float64))
+
+
+def _packed_grad(cfg, cq):
+    rng = np.random.default_rng(cfg.seed + 100)
+    return rng.standard_normal((int(cq[-1]), cfg.Hq, cfg.d))
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, None), (True, 4)])
+def test_packed_backward_equals_dense_per_document(causal, window):
+    cfg = _cfg(Hq=4, Hkv=2, d=6)
+    lq, lk = [9, 1, 14], ([9, 1, 14] if causal else [12, 3, 5])
+    Q, K, V, cq, ck = inputs.make_packed(cfg, lq, lk)
+    dO = _packed_grad(cfg, cq)
+    O, L = oracle.varlen_attention(Q, K, V, cq, ck, causal, 0.5, window)
+    dQ, dK, dV = oracle.varlen_backward(Q, K, V, O, L, dO, cq, ck, causal, 0.5, window)
+    for b in range(3):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        tr = lambda x, a, c: np.asarray(x[a:c]).transpose(1, 0, 2)[None]
+        rq, rk, rv = oracle.dense_backward(tr(Q, q0, q1), tr(K, k0, k1), tr(V, k0, k1),
+                                           tr(dO, q0, q1), causal, 0.5, window)
+        assert np.max(np.abs(dQ[q0:q1] - rq[0].transpose(1, 0, 2))) <= 1e-12
+        assert np.max(np.abs(dK[k0:k1] - rk[0].transpose(1, 0, 2))) <= 1e-12
+        assert np.max(np.abs(dV[k0:k1] - rv[0].transpose(1, 0, 2))) <= 1e-12
+
+
+def test_packed_backward_against_finite_differences():
+    # central differences of sum(dO * O) over the whole packed output
+    cfg = _cfg(Hq=2, Hkv=1, d=3)
+    Q, K, V, cq, ck = inputs.make_packed(cfg, [6, 2, 5], [8, 2, 5])
+    Q, K, V = (x.astype(np.float64) for x in (Q, K, V))
+    dO = _packed_grad(cfg, cq)
+    O, L = oracle.varlen_attention(Q, K, V, cq, ck, True, 0.7)
+    dQ, dK, dV = oracle.varlen_backward(Q, K, V, O, L, dO, cq, ck, True, 0.7)
+    eps = 1e-5
+    for x, g, idx in ((Q, dQ, (3, 1, 2)), (Q, dQ, (7, 0, 0)), (K, dK, (1, 0, 1)),
+                      (K, dK, (12, 0, 2)), (V, dV, (0, 0, 0)), (V, dV, (9, 0, 1))):
+        keep = x[idx]
+        x[idx] = keep + eps
+        fp = np.sum(dO * oracle.varlen_attention(Q, K, V, cq, ck, True, 0.7)[0])
+        x[idx] = keep - eps
+        fm = np.sum(dO * oracle.varlen_attention(Q, K, V, cq, ck, True, 0.7)[0])
+        x[idx] = keep
+        assert abs((fp - fm) / (2 * eps) - g[idx]) < 1e-7, idx
+
+
+def test_packed_backward_rows_without_keys():
+    cfg = _cfg(Hq=2, Hkv=1, d=4)
+    Q, K, V, cq, ck = inputs.make_packed(cfg, [6, 3], [4, 0])
+    dO = _packed_grad(cfg, cq)
+    O, L = oracle.varlen_attention(Q, K, V, cq, ck, True)
+    dQ, dK, dV = oracle.varlen_backward(Q, K, V, O, L, dO, cq, ck, True)
+    assert not dQ[0:2].any() and not dQ[6:9].any() and dQ[2:6].any()
+    assert np.all(np.isfinite(dK)) and np.all(np.isfinite(dV))
