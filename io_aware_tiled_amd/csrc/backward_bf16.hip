@@ -138,9 +138,17 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int hf = lane >> 5;
 
   const int nqb = (Tq + S::BR - 1) / S::BR;
-  const int lin = xcd_order(blockIdx.x, gridDim.x);
-  const int bh = lin / nqb;
+  // Dense batches: each XCD a contiguous range of (head, query block) work. Packed batches,
+  // whose sequences differ in length: query-block-major, longest blocks first, dealt round-robin
+  // to the XCDs, so no XCD is left with one long sequence.
+  const int lin = VARLEN ? (int)blockIdx.x : xcd_order(blockIdx.x, gridDim.x);
+  const int nbh = gridDim.x / nqb;
+  int bh = lin / nqb;
   int qb = lin - bh * nqb;
+  if (VARLEN) {
+    bh = lin % nbh;
+    qb = lin / nbh;
+  }
   if (causal) qb = nqb - 1 - qb;  // longest causal blocks first
   const int b = bh / Hq;
   const int h = bh - b * Hq;
@@ -372,9 +380,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   const int hf = lane >> 5;
 
   const int nkb = (Tk + BK - 1) / BK;
-  const int lin = xcd_order(blockIdx.x, gridDim.x);
-  const int bg = lin / nkb;
-  const int kb = lin - bg * nkb;  // ascending: the longest causal blocks first
+  // grid order as in the dQ kernel: key-block-major for packed batches
+  const int lin = VARLEN ? (int)blockIdx.x : xcd_order(blockIdx.x, gridDim.x);
+  const int nbg = gridDim.x / nkb;
+  const int bg = VARLEN ? lin % nbg : lin / nkb;
+  const int kb = VARLEN ? lin / nbg : lin - bg * nkb;  // ascending: longest causal blocks first
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
   const int G = Hq / Hkv;
