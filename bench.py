@@ -550,7 +550,8 @@ def main():
             "backward": {"ms": round(vb["median"], 4), "tflops": round(vb_tflops, 2),
                          "pct_mfma_peak": round(100 * vb_tflops / PEAK_BF16_TFLOPS, 2),
                          "flops_per_call": vb_flops, "ms_stats": _r(vb),
-                         "work": "2.5 times the forward count: the five backward products"},
+                         "work": "2.5 times the forward count: the five backward products",
+                         "traffic": traffic_for("backward_bf16.hip", "backward_varlen")},
         },
         "paged_decode": {
             "workload": "GQA decode bf16 B=64 Hq=64 Hkv=8 Tk=8192 d=128 over a paged cache, "
