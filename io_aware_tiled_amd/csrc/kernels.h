@@ -39,11 +39,12 @@ struct Packed {
   int total_q, total_k;
 };
 
-// bf16 matrix-core prefill over a packed batch (64-key tiles, 8 waves): p.B is the number of
-// sequences, p.Tq and p.Tk the longest lengths (the grid covers p.Tq rows per sequence; longer
-// sequences are cut there), LSE is [Hq, total_q].
-hipError_t launch_prefill_varlen_bf16(const Problem& p, const Packed& pk, int schedule,
-                                      hipStream_t stream);
+// bf16 matrix-core prefill over a packed batch: p.B is the number of sequences, p.Tq and p.Tk
+// the longest lengths (the grid covers p.Tq rows per sequence; longer sequences are cut there),
+// LSE is [Hq, total_q]. block_kv, waves as for launch_prefill_bf16; schedule 3 is the
+// query-block-major order that balances sequences of different lengths.
+hipError_t launch_prefill_varlen_bf16(const Problem& p, const Packed& pk, int block_kv,
+                                      int waves, int schedule, hipStream_t stream);
 
 // fp32 vector-ALU path, any Tq (also Tq == 1), d in {32, 64, 128}.
 hipError_t launch_prefill_f32(const Problem& p, hipStream_t stream);

@@ -396,8 +396,11 @@ hipError_t launch_t(const Problem& p, int schedule, const Packed* pk, hipStream_
 template <int D>
 hipError_t launch_d(const Problem& p, int block_kv, int waves, int schedule, const Packed* pk,
                     hipStream_t stream) {
-  if (pk) {  // packed batches use one configuration per head dim
+  if (pk) {
+    if (block_kv == 64 && waves == 4) return launch_t<D, 64, 4, true>(p, schedule, pk, stream);
     if (block_kv == 64 && waves == 8) return launch_t<D, 64, 8, true>(p, schedule, pk, stream);
+    if (block_kv == 32 && waves == 4) return launch_t<D, 32, 4, true>(p, schedule, pk, stream);
+    if (block_kv == 32 && waves == 8) return launch_t<D, 32, 8, true>(p, schedule, pk, stream);
     return hipErrorInvalidValue;
   }
   if (block_kv == 64 && waves == 4) return launch_t<D, 64, 4, false>(p, schedule, pk, stream);
@@ -424,9 +427,9 @@ hipError_t launch_prefill_bf16(const Problem& p, int block_kv, int waves, int sc
   return launch_any(p, block_kv, waves, schedule, nullptr, stream);
 }
 
-hipError_t launch_prefill_varlen_bf16(const Problem& p, const Packed& pk, int schedule,
-                                      hipStream_t stream) {
-  return launch_any(p, 64, 8, schedule, &pk, stream);  // schedule 3 by default (api.cpp)
+hipError_t launch_prefill_varlen_bf16(const Problem& p, const Packed& pk, int block_kv,
+                                      int waves, int schedule, hipStream_t stream) {
+  return launch_any(p, block_kv, waves, schedule, &pk, stream);
 }
 
 }  // namespace fattn

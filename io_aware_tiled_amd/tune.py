@@ -23,10 +23,18 @@ import io_aware_tiled_amd as fa
 PREFILL_SHAPES = [
     # B, Hq, Hkv, T, d, causal
     (1, 32, 32, 8192, 128, True),
+    (1, 32, 32, 8192, 128, False),
+    (1, 32, 32, 4096, 128, True),
     (1, 32, 32, 4096, 128, False),
+    (4, 32, 32, 2048, 128, True),
+    (16, 32, 32, 1024, 128, True),
+    (16, 32, 32, 1024, 128, False),
     (2, 32, 8, 16384, 128, True),
     (4, 16, 16, 1024, 64, True),
-    (1, 32, 32, 8192, 64, True),
+    (4, 16, 16, 1024, 64, False),
+    (16, 32, 32, 1024, 64, True),
+    (2, 32, 32, 8192, 64, True),
+    (2, 32, 32, 8192, 64, False),
 ]
 DECODE_SHAPES = [
     # B, Hq, Hkv, Tk, d
