@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "grid_order.h"
 #include "lds_tiles.h"
 
 namespace fattn {
@@ -108,15 +109,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict_
   }
 }
 
-// Workgroup order shared by both gradient kernels: workgroups are dealt round-robin to the 8
-// XCDs, so give each XCD a contiguous range of the logical order (the blocks of one head then
-// share that XCD's L2).
-__device__ __forceinline__ int xcd_order(int lin, int total) {
-  const int xcd = lin & 7, k = lin >> 3;
-  const int q8 = total >> 3, r8 = total & 7;
-  return xcd * q8 + (xcd < r8 ? xcd : r8) + k;
-}
-
 // ---- dQ: one workgroup per (batch, query head, block of 32 * NW query rows).
 // VARLEN: packed batch (Q, dO, dQ [total_q, Hq, D], K, V [total_k, Hkv, D], the workspace of
 // bwd_prep_packed_kernel); blockIdx covers (sequence, head, query block) with Tq and Tk the
@@ -138,16 +130,15 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int hf = lane >> 5;
 
   const int nqb = (Tq + S::BR - 1) / S::BR;
-  // Dense batches: each XCD a contiguous range of (head, query block) work. Packed batches,
-  // whose sequences differ in length: query-block-major, longest blocks first, dealt round-robin
-  // to the XCDs, so no XCD is left with one long sequence.
-  const int lin = VARLEN ? (int)blockIdx.x : xcd_order(blockIdx.x, gridDim.x);
-  const int nbh = gridDim.x / nqb;
-  int bh = lin / nqb;
-  int qb = lin - bh * nqb;
+  // Dense batches: each XCD a contiguous range of (head, query block) work. Packed batches, whose
+  // sequences differ in length: pairs dealt to the XCDs by head, each pair's blocks together.
+  int bh, qb;
   if (VARLEN) {
-    bh = lin % nbh;
-    qb = lin / nbh;
+    xcd_grouped_pairs(blockIdx.x, gridDim.x / nqb, nqb, bh, qb);
+  } else {
+    const int lin = xcd_contiguous(blockIdx.x, gridDim.x);
+    bh = lin / nqb;
+    qb = lin - bh * nqb;
   }
   if (causal) qb = nqb - 1 - qb;  // longest causal blocks first
   const int b = bh / Hq;
@@ -380,11 +371,15 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   const int hf = lane >> 5;
 
   const int nkb = (Tk + BK - 1) / BK;
-  // grid order as in the dQ kernel: key-block-major for packed batches
-  const int lin = VARLEN ? (int)blockIdx.x : xcd_order(blockIdx.x, gridDim.x);
-  const int nbg = gridDim.x / nkb;
-  const int bg = VARLEN ? lin % nbg : lin / nkb;
-  const int kb = VARLEN ? lin / nbg : lin - bg * nkb;  // ascending: longest causal blocks first
+  // grid order as in the dQ kernel; key blocks ascending: longest causal blocks first
+  int bg, kb;
+  if (VARLEN) {
+    xcd_grouped_pairs(blockIdx.x, gridDim.x / nkb, nkb, bg, kb);
+  } else {
+    const int lin = xcd_contiguous(blockIdx.x, gridDim.x);
+    bg = lin / nkb;
+    kb = lin - bg * nkb;
+  }
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
   const int G = Hq / Hkv;
@@ -612,11 +607,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
     }
 }
 
-template <int D>
-hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_t stream) {
-  const int BH = p.B * p.Hq;
-  const int nqt = (p.Tq + 31) / 32;
-  const float c = p.scale * kLog2eF;
+// dQ and dK/dV launches with DQ_NW waves per dQ workgroup (32 * DQ_NW query rows) and KV_NW
+// waves per dK/dV workgroup (32 * KV_NW keys).
+template <int D, int DQ_NW, int KV_NW>
+hipError_t launch_grads(const BwdProblem& p, const Packed* pk, float* ws, float c,
+                        hipStream_t stream) {
   const __bf16* Q = static_cast<const __bf16*>(p.Q);
   const __bf16* K = static_cast<const __bf16*>(p.K);
   const __bf16* V = static_cast<const __bf16*>(p.V);
@@ -624,22 +619,9 @@ hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_
   const int* cu_q = pk ? pk->cu_q : nullptr;
   const int* cu_k = pk ? pk->cu_k : nullptr;
   const int total_q = pk ? pk->total_q : 0, total_k = pk ? pk->total_k : 0;
-
-  constexpr int RPB = 256 / (D / 8);
-  if (pk) {
-    const long long rows = (long long)p.Hq * total_q;
-    bwd_prep_packed_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                                stream>>>(static_cast<const __bf16*>(p.O), dO, p.LSE, ws, p.Hq,
-                                          total_q);
-  } else {
-    const long long rows = (long long)BH * nqt * 32;
-    bwd_prep_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(
-        static_cast<const __bf16*>(p.O), dO, p.LSE, ws, BH, p.Tq, nqt);
-  }
-
-  constexpr int DQ_NW = 8, DQ_BC = 32;
+  constexpr int DQ_BC = 32;
   const int nqb = (p.Tq + 32 * DQ_NW - 1) / (32 * DQ_NW);
-  const dim3 dq_grid((unsigned)(BH * nqb)), dq_block(64 * DQ_NW);
+  const dim3 dq_grid((unsigned)(p.B * p.Hq * nqb)), dq_block(64 * DQ_NW);
   if (pk)
     bwd_dq_kernel<D, DQ_BC, DQ_NW, true><<<dq_grid, dq_block, 0, stream>>>(
         Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
@@ -649,7 +631,7 @@ hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_
         Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
         p.window, p.scale, c, nullptr, nullptr, 0, 0);
 
-  constexpr int KV_NW = 4, KV_BC = 32, KV_MINW = D >= 128 ? 1 : 2;
+  constexpr int KV_BC = 32, KV_MINW = D >= 128 ? 1 : 2;
   const int nkb = (p.Tk + 32 * KV_NW - 1) / (32 * KV_NW);
   const dim3 kv_grid((unsigned)(p.B * p.Hkv * nkb)), kv_block(64 * KV_NW);
   if (pk)
@@ -661,6 +643,34 @@ hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_
         Q, K, V, dO, ws, static_cast<__bf16*>(p.dK), static_cast<__bf16*>(p.dV), p.Hq, p.Hkv,
         p.Tq, p.Tk, p.causal, p.window, p.scale, c, nullptr, nullptr, 0, 0);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_t stream) {
+  const int BH = p.B * p.Hq;
+  const int nqt = (p.Tq + 31) / 32;
+  const float c = p.scale * kLog2eF;
+  const __bf16* dO = static_cast<const __bf16*>(p.dO);
+
+  constexpr int RPB = 256 / (D / 8);
+  if (pk) {
+    const long long rows = (long long)p.Hq * pk->total_q;
+    bwd_prep_packed_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                                stream>>>(static_cast<const __bf16*>(p.O), dO, p.LSE, ws, p.Hq,
+                                          pk->total_q);
+  } else {
+    const long long rows = (long long)BH * nqt * 32;
+    bwd_prep_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(
+        static_cast<const __bf16*>(p.O), dO, p.LSE, ws, BH, p.Tq, nqt);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // Dense batches: 4-wave dQ workgroups (128 query rows) and 2-wave dK/dV workgroups (64 keys),
+  // 4-29% faster than 8 and 4 waves on causal d = 64 and 128 at T = 1024-4096 (more workgroups
+  // for the 256 CUs) and no slower at T = 8192. Packed batches keep 8 and 4 waves: their many
+  // early-exiting workgroups of short documents made the smaller shape 7% slower on 8 documents.
+  if (!pk) return launch_grads<D, 4, 2>(p, pk, ws, c, stream);
+  return launch_grads<D, 8, 4>(p, pk, ws, c, stream);
 }
 
 hipError_t launch_any(const BwdProblem& p, const Packed* pk, float* ws, hipStream_t stream) {

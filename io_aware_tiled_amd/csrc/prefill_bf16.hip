@@ -35,6 +35,7 @@
 #include <cstdint>
 
 #include "kernels.h"
+#include "grid_order.h"
 #include "lds_tiles.h"
 
 namespace fattn {
@@ -70,27 +71,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   // ---- which (batch, head, query block) this workgroup owns
   const int nqb = (Tq + S::BR - 1) / S::BR;
   const int total = gridDim.x;
-  int lin = blockIdx.x;
-  if (schedule == 2) {
-    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous range of the
-    // logical order so the query blocks of one head share that XCD's L2 for K and V.
-    const int xcd = lin & 7, k = lin >> 3;
-    const int q8 = total >> 3, r8 = total & 7;
-    lin = xcd * q8 + (xcd < r8 ? xcd : r8) + k;
-  }
+  const int lin = schedule == 2 ? xcd_contiguous(blockIdx.x, total) : (int)blockIdx.x;
   int bh = lin / nqb;
   int qb = lin - bh * nqb;
-  if (schedule == 2 && causal) qb = nqb - 1 - qb;  // longest causal blocks first
-  if (schedule == 3) {
-    // Query-block-major, longest causal blocks first across all (batch, head) pairs, dealt
-    // round-robin to the XCDs as dispatched: every XCD gets an even share of every block size.
-    // For packed batches, whose documents differ in length, where a head-contiguous range per
-    // XCD would give one XCD one document.
-    const int nbh = total / nqb;
-    bh = lin % nbh;
-    qb = lin / nbh;
-    if (causal) qb = nqb - 1 - qb;
-  }
+  // schedule 3, for packed batches: pairs grouped by XCD, each pair's blocks together
+  if (schedule == 3) xcd_grouped_pairs(blockIdx.x, total / nqb, nqb, bh, qb);
+  if (schedule >= 2 && causal) qb = nqb - 1 - qb;  // longest causal blocks first
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int g = h / (Hq / Hkv);
