@@ -665,11 +665,12 @@ hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Dense batches: 4-wave dQ workgroups (128 query rows) and 2-wave dK/dV workgroups (64 keys),
-  // 4-29% faster than 8 and 4 waves on causal d = 64 and 128 at T = 1024-4096 (more workgroups
-  // for the 256 CUs) and no slower at T = 8192. Packed batches keep 8 and 4 waves: their many
-  // early-exiting workgroups of short documents made the smaller shape 7% slower on 8 documents.
-  if (!pk) return launch_grads<D, 4, 2>(p, pk, ws, c, stream);
+  // 4-wave dQ workgroups (128 query rows) and 2-wave dK/dV workgroups (64 keys): against 8 and
+  // 4 waves, more workgroups for the 256 CUs, 4-29% faster on dense causal d = 64 and 128 at
+  // T = 1024-4096 and no slower at T = 8192, and 5% faster on a packed batch of 35 documents up
+  // to 4096 tokens. Packed batches with longer sequences keep 8 and 4 waves (3% faster on 8
+  // documents up to 8192 tokens: half the re-reads of Q and dO per key).
+  if (!pk || p.Tk <= 4096) return launch_grads<D, 4, 2>(p, pk, ws, c, stream);
   return launch_grads<D, 8, 4>(p, pk, ws, c, stream);
 }
 
