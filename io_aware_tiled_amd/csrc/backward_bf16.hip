@@ -665,12 +665,16 @@ hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 4-wave dQ workgroups (128 query rows) and 2-wave dK/dV workgroups (64 keys): against 8 and
-  // 4 waves, more workgroups for the 256 CUs, 4-29% faster on dense causal d = 64 and 128 at
-  // T = 1024-4096 and no slower at T = 8192, and 5% faster on a packed batch of 35 documents up
-  // to 4096 tokens. Packed batches with longer sequences keep 8 and 4 waves (3% faster on 8
-  // documents up to 8192 tokens: half the re-reads of Q and dO per key).
-  if (!pk || p.Tk <= 4096) return launch_grads<D, 4, 2>(p, pk, ws, c, stream);
+  // Workgroup size by the keys an average row sees (half the longest sequence when causal, at
+  // most the window). Up to 2048: 4-wave dQ workgroups (128 query rows) and 2-wave dK/dV
+  // workgroups (64 keys), whose doubled workgroup count balances the CUs better, against 8 and
+  // 4 waves 16-21% faster on causal d = 64 and 128 at T = 1024 and 2048 and 5% on a packed
+  // batch of 35 documents up to 4096 tokens. Beyond, 8 and 4 waves, which read Q and dO (K and
+  // V) half as often per key (query row): 3% faster on non-causal d = 128 from T = 4096 on and
+  // on a packed batch of 8 documents up to 8192 tokens, equal on causal T = 8192.
+  long long seen = p.causal ? p.Tk / 2 : p.Tk;
+  if (p.window > 0 && p.window < seen) seen = p.window;
+  if (seen <= 2048) return launch_grads<D, 4, 2>(p, pk, ws, c, stream);
   return launch_grads<D, 8, 4>(p, pk, ws, c, stream);
 }
 
