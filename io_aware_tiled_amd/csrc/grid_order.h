@@ -17,6 +17,34 @@ __device__ __forceinline__ int xcd_contiguous(int id, int total) {
   return xcd * q8 + (xcd < r8 ? xcd : r8) + k;
 }
 
+// Dense batches, causal blocks of different sizes: XCD x gets the same contiguous range of whole
+// pairs as with xcd_contiguous, but within it the pairs are taken G at a time and the blocks of
+// those G pairs run block-major (block 0 of each, then block 1, ...). Workgroups are dispatched
+// in order as CUs free up, so a long causal block dispatched next to blocks of its own size
+// (rather than next to a whole pair's mix of sizes) keeps the CUs of an XCD finishing together;
+// G pairs at a time keep the K and V (or Q and dO) those blocks read few enough to share L2.
+// Ranges that do not cover whole pairs (pair counts not a multiple of 8) fall back to
+// xcd_contiguous. `id` is blockIdx over `total` = nbh * nblk blocks.
+template <int G>
+__device__ __forceinline__ void xcd_pair_groups(int id, int total, int nblk, int& bh, int& blk) {
+  const int x = id & 7, k = id >> 3;
+  const int q8 = total >> 3, r8 = total & 7;
+  const int nx = q8 + (x < r8 ? 1 : 0);
+  const int sx = x * q8 + (x < r8 ? x : r8);
+  if (sx % nblk != 0 || nx % nblk != 0) {
+    const int lin = sx + k;
+    bh = lin / nblk;
+    blk = lin - bh * nblk;
+    return;
+  }
+  const int pairs = nx / nblk;
+  const int grp = k / (G * nblk);
+  const int w = k - grp * (G * nblk);
+  const int in_grp = min(G, pairs - grp * G);
+  bh = sx / nblk + grp * G + w % in_grp;
+  blk = w / in_grp;
+}
+
 // Packed batches, whose sequences differ in length: a contiguous range of pairs would hand one
 // XCD one long sequence. Instead pair bh goes to XCD bh mod 8 (pairs are sequence-major, so with
 // a head count that is a multiple of 8 every XCD gets every sequence, with an eighth of its

@@ -71,9 +71,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   // ---- which (batch, head, query block) this workgroup owns
   const int nqb = (Tq + S::BR - 1) / S::BR;
   const int total = gridDim.x;
-  const int lin = schedule == 2 ? xcd_contiguous(blockIdx.x, total) : (int)blockIdx.x;
-  int bh = lin / nqb;
-  int qb = lin - bh * nqb;
+  int bh = (int)blockIdx.x / nqb;
+  int qb = (int)blockIdx.x - bh * nqb;
+  // schedule 2: whole heads per XCD, 8 heads at a time query-block-major
+  if (schedule == 2) xcd_pair_groups<8>(blockIdx.x, total, nqb, bh, qb);
   // schedule 3, for packed batches: pairs grouped by XCD, each pair's blocks together
   if (schedule == 3) xcd_grouped_pairs(blockIdx.x, total / nqb, nqb, bh, qb);
   if (schedule >= 2 && causal) qb = nqb - 1 - qb;  // longest causal blocks first
