@@ -130,15 +130,14 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int hf = lane >> 5;
 
   const int nqb = (Tq + S::BR - 1) / S::BR;
-  // Dense batches: each XCD a contiguous range of (head, query block) work. Packed batches, whose
-  // sequences differ in length: pairs dealt to the XCDs by head, each pair's blocks together.
+  // Dense batches: each XCD a contiguous range of whole heads, 4 heads at a time block-major
+  // (blocks of one size dispatched together). Packed batches, whose sequences differ in length:
+  // pairs dealt to the XCDs by head, each pair's blocks together.
   int bh, qb;
   if (VARLEN) {
     xcd_grouped_pairs(blockIdx.x, gridDim.x / nqb, nqb, bh, qb);
   } else {
-    const int lin = xcd_contiguous(blockIdx.x, gridDim.x);
-    bh = lin / nqb;
-    qb = lin - bh * nqb;
+    xcd_pair_groups<4>(blockIdx.x, gridDim.x, nqb, bh, qb);
   }
   if (causal) qb = nqb - 1 - qb;  // longest causal blocks first
   const int b = bh / Hq;
@@ -376,9 +375,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   if (VARLEN) {
     xcd_grouped_pairs(blockIdx.x, gridDim.x / nkb, nkb, bg, kb);
   } else {
-    const int lin = xcd_contiguous(blockIdx.x, gridDim.x);
-    bg = lin / nkb;
-    kb = lin - bg * nkb;
+    xcd_pair_groups<4>(blockIdx.x, gridDim.x, nkb, bg, kb);
   }
   const int b = bg / Hkv;
   const int g = bg - b * Hkv;
