@@ -21,23 +21,27 @@ struct PrefillEntry {
   int schedule;
 };
 
-// Measured on MI355X with `python -m io_aware_tiled_amd.tune` (TFLOP/s of the best entry against
-// the next best in parentheses where it matters):
-//  * d = 128, causal: 4 waves (128 query rows per workgroup) up to Tk = 4096 (T = 1024: 572 vs
-//    456 with 8 waves; 4096: 836 vs 712), 8 waves beyond (8192: 1072 vs 1019).
-//  * d = 128, no mask: 4 waves up to Tk = 1024 (880 vs 830), 8 waves beyond.
-//  * d = 64, causal: 4 waves with 64-key tiles (T = 8192: 852 vs 757 with 8 waves).
+// Measured on MI355X with `python -m io_aware_tiled_amd.tune` and the head-group grid order
+// (TFLOP/s of the chosen entry against the next best in parentheses where it matters):
+//  * d = 128, causal: 4 waves (128 query rows per workgroup) up to Tk = 2048 (B = 1, T = 2048:
+//    633 vs 541 with 8 waves; B = 16, T = 1024: 635 vs 604), 8 waves beyond (B = 1, T = 4096:
+//    966 vs 913; T = 8192: 1108 vs 1074).
+//  * d = 128, no mask: 4 waves up to Tk = 1024 (887 vs 860), 8 waves beyond.
+//  * d = 64, causal: 64-key tiles with 4 waves up to Tk = 1024 (B = 4, H = 16: 302 vs 296),
+//    32-key tiles with 4 waves beyond (T = 2048 to 16384 with 32 heads: 2-3% faster, e.g.
+//    T = 8192: 940 vs 922).
 //  * d = 64, no mask: 32-key tiles with 4 waves up to Tk = 1024, with 8 waves beyond
-//    (T = 8192: 995 vs 968).
+//    (T = 2048: 932 vs 908; T = 8192: 1008 vs 975).
 // 64-key tiles win everywhere else; the XCD-grouped, longest-first order is 1.3-1.5x faster
 // than row-major for causal masks and no slower without one.
 static const PrefillEntry kPrefillTable[] = {
     // d, causal, tk_max, block_kv, waves, schedule
-    {128, 1, 4096, 64, 4, 2},
+    {128, 1, 2048, 64, 4, 2},
     {128, 1, 0, 64, 8, 2},
     {128, 0, 1024, 64, 4, 2},
     {128, 0, 0, 64, 8, 2},
-    {64, 1, 0, 64, 4, 2},
+    {64, 1, 1024, 64, 4, 2},
+    {64, 1, 0, 32, 4, 2},
     {64, 0, 1024, 32, 4, 2},
     {64, 0, 0, 32, 8, 2},
     {32, -1, 0, 64, 4, 2},
