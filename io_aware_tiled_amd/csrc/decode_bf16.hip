@@ -179,11 +179,13 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
   Block<D> cur;
   if (kbeg < kend) load_block<D>(cur, Kh, Vh, halves_of<PAGED>(kbeg, kend, pm), kbeg, kend, lane);
 
+  // page lookups run one block ahead of the loads that use them
+  Halves hv_next = halves_of<PAGED>(kbeg + KB, kend, pm);
   for (int kb = kbeg; kb < kend; kb += KB) {
     const bool more = kb + KB < kend;
     Block<D> nxt;
-    if (more)
-      load_block<D>(nxt, Kh, Vh, halves_of<PAGED>(kb + KB, kend, pm), kb + KB, kend, lane);
+    if (more) load_block<D>(nxt, Kh, Vh, hv_next, kb + KB, kend, lane);
+    hv_next = halves_of<PAGED>(kb + 2 * KB, kend, pm);
 
     __syncthreads();  // the previous block's V^T reads are done
     if (lane < D / 2) {
