@@ -48,9 +48,22 @@ __device__ __forceinline__ void xcd_pair_groups(int id, int total, int nblk, int
 // Packed batches, whose sequences differ in length: a contiguous range of pairs would hand one
 // XCD one long sequence. Instead pair bh goes to XCD bh mod 8 (pairs are sequence-major, so with
 // a head count that is a multiple of 8 every XCD gets every sequence, with an eighth of its
-// heads) and, within an XCD, the pairs run one after another with their blocks together.
+// heads). Within an XCD the pairs run G at a time, the blocks of those G pairs block-major, as
+// in xcd_pair_groups (G = 1: each pair's blocks together). Pair counts that are not a multiple
+// of 8 keep the deal by bh mod 8 with G = 1.
 // `id` is blockIdx over nbh pairs of nblk blocks; returns the pair and the block index within it.
+template <int G>
 __device__ __forceinline__ void xcd_grouped_pairs(int id, int nbh, int nblk, int& bh, int& blk) {
+  if ((nbh & 7) == 0) {
+    // XCD x runs exactly the nbh / 8 pairs x, x + 8, ...: the k-th workgroup it is dealt
+    const int x = id & 7, k = id >> 3, px = nbh >> 3;
+    const int grp = k / (G * nblk);
+    const int w = k - grp * (G * nblk);
+    const int in_grp = min(G, px - grp * G);
+    bh = x + 8 * (grp * G + w % in_grp);
+    blk = w / in_grp;
+    return;
+  }
   const int lin = xcd_contiguous(id, nbh * nblk);
   const int pos = lin / nblk;  // position in the order of pairs grouped by bh mod 8
   blk = lin - pos * nblk;

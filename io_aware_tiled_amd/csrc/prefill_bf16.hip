@@ -75,8 +75,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   int qb = (int)blockIdx.x - bh * nqb;
   // schedule 2: whole heads per XCD, 8 heads at a time query-block-major
   if (schedule == 2) xcd_pair_groups<8>(blockIdx.x, total, nqb, bh, qb);
-  // schedule 3, for packed batches: pairs grouped by XCD, each pair's blocks together
-  if (schedule == 3) xcd_grouped_pairs(blockIdx.x, total / nqb, nqb, bh, qb);
+  // schedule 3, for packed batches: pairs dealt to the XCDs by head, 4 at a time block-major
+  if (schedule == 3) xcd_grouped_pairs<4>(blockIdx.x, total / nqb, nqb, bh, qb);
   if (schedule >= 2 && causal) qb = nqb - 1 - qb;  // longest causal blocks first
   const int b = bh / Hq;
   const int h = bh - b * Hq;
