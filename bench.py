@@ -44,8 +44,8 @@ if ROOT not in sys.path:
 METRIC = "causal prefill TFLOP/s (% MFMA peak) at T=8192,d=128; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
-PREFILL = "c3_bf16_causal_t8192_d128"
-DECODE = "c4_bf16_gqa_decode_tk8192_d128"
+PREFILL = "bf16_causal_b1_h32_t8192_d128"
+DECODE = "bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128"
 PROFILES = os.path.join(ROOT, "profiles")
 
 

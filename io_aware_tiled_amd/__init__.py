@@ -21,8 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libfattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fattn.h")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python io_aware_tiled_amd/build.py` "
-                      "(or __graft_entry__.build()) first")
+    raise ImportError(f"{LIB_PATH} is not built: run `python io_aware_tiled_amd/build.py` first")
 
 # torch is imported first so that its bundled HIP runtime is the one in the process: libfattn
 # needs libamdhip64.so.7 by soname and then binds to that same runtime, which is the one that

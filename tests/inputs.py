@@ -67,26 +67,26 @@ class AttnConfig:
 
 # The five workloads the method is measured on, plus the two prefill variants of the T=8192 case.
 CONFIGS = {
-    "c1_f32_causal_t128_d32": AttnConfig(
-        "c1_f32_causal_t128_d32", B=1, Hq=4, Hkv=4, Tq=128, Tk=128, d=32,
+    "f32_causal_b1_h4_t128_d32": AttnConfig(
+        "f32_causal_b1_h4_t128_d32", B=1, Hq=4, Hkv=4, Tq=128, Tk=128, d=32,
         dtype="f32", causal=True, dist="normal", seed=0),
-    "c2_bf16_causal_t1024_d64": AttnConfig(
-        "c2_bf16_causal_t1024_d64", B=4, Hq=16, Hkv=16, Tq=1024, Tk=1024, d=64,
+    "bf16_causal_b4_h16_t1024_d64": AttnConfig(
+        "bf16_causal_b4_h16_t1024_d64", B=4, Hq=16, Hkv=16, Tq=1024, Tk=1024, d=64,
         dtype="bf16", causal=True, dist="uniform08", seed=42),
-    "c3_bf16_causal_t8192_d128": AttnConfig(
-        "c3_bf16_causal_t8192_d128", B=1, Hq=32, Hkv=32, Tq=8192, Tk=8192, d=128,
+    "bf16_causal_b1_h32_t8192_d128": AttnConfig(
+        "bf16_causal_b1_h32_t8192_d128", B=1, Hq=32, Hkv=32, Tq=8192, Tk=8192, d=128,
         dtype="bf16", causal=True, dist="normal", seed=1),
-    "c3_bf16_noncausal_t4096_d128": AttnConfig(
-        "c3_bf16_noncausal_t4096_d128", B=1, Hq=32, Hkv=32, Tq=4096, Tk=4096, d=128,
+    "bf16_noncausal_b1_h32_t4096_d128": AttnConfig(
+        "bf16_noncausal_b1_h32_t4096_d128", B=1, Hq=32, Hkv=32, Tq=4096, Tk=4096, d=128,
         dtype="bf16", causal=False, dist="normal", seed=2),
-    "c3_bf16_causal_t8000_d128": AttnConfig(
-        "c3_bf16_causal_t8000_d128", B=1, Hq=32, Hkv=32, Tq=8000, Tk=8000, d=128,
+    "bf16_causal_b1_h32_t8000_d128": AttnConfig(
+        "bf16_causal_b1_h32_t8000_d128", B=1, Hq=32, Hkv=32, Tq=8000, Tk=8000, d=128,
         dtype="bf16", causal=True, dist="normal", seed=3),
-    "c4_bf16_gqa_decode_tk8192_d128": AttnConfig(
-        "c4_bf16_gqa_decode_tk8192_d128", B=64, Hq=64, Hkv=8, Tq=1, Tk=8192, d=128,
+    "bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128": AttnConfig(
+        "bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128", B=64, Hq=64, Hkv=8, Tq=1, Tk=8192, d=128,
         dtype="bf16", causal=False, dist="normal", seed=4),
-    "c5_bf16_gqa_causal_t16384_d128": AttnConfig(
-        "c5_bf16_gqa_causal_t16384_d128", B=2, Hq=32, Hkv=8, Tq=16384, Tk=16384, d=128,
+    "bf16_gqa_causal_b2_hq32_hkv8_t16384_d128": AttnConfig(
+        "bf16_gqa_causal_b2_hq32_hkv8_t16384_d128", B=2, Hq=32, Hkv=8, Tq=16384, Tk=16384, d=128,
         dtype="bf16", causal=True, dist="normal", seed=5, k_spike=(0.01, 8.0)),
 }
 

@@ -144,9 +144,9 @@ def test_keys_no_row_sees_have_zero_gradients(fa):
     assert dk[:, :, first_seen:].any()
 
 
-def test_workload_c2_full(fa):
+def test_causal_b4_h16_t1024_d64_full(fa):
     # B=4, H=16, T=1024, d=64, U(-0.8, 0.8), causal: every gradient element against the oracle.
-    cfg = inputs.CONFIGS["c2_bf16_causal_t1024_d64"]
+    cfg = inputs.CONFIGS["bf16_causal_b4_h16_t1024_d64"]
     _say(cfg.name)
     bwd_case(fa, cfg)
 
@@ -226,17 +226,17 @@ def sampled_e2e(fa, cfg: AttnConfig, q_heads, kv_heads):
         check_grad(_np(dv[b, g, keys]), rv, f"{cfg.name} dV ({b},{g})")
 
 
-def test_workload_c3_sampled(fa):
+def test_causal_t8192_d128_sampled(fa):
     # B=1, H=32, T=8192, d=128, causal: the forward's headline shape.
-    sampled_e2e(fa, inputs.CONFIGS["c3_bf16_causal_t8192_d128"], [(0, 0), (0, 31)], [(0, 7)])
+    sampled_e2e(fa, inputs.CONFIGS["bf16_causal_b1_h32_t8192_d128"], [(0, 0), (0, 31)], [(0, 7)])
 
 
-def test_workload_c3_ragged_noncausal_sampled(fa):
-    cfg = inputs.CONFIGS["c3_bf16_causal_t8000_d128"].replace(causal=False, name="c3 t8000 nc")
+def test_noncausal_t8000_d128_sampled(fa):
+    cfg = inputs.CONFIGS["bf16_causal_b1_h32_t8000_d128"].replace(causal=False, name="noncausal t8000")
     sampled_e2e(fa, cfg, [(0, 5)], [(0, 20)])
 
 
-def test_workload_c5_sampled(fa):
+def test_gqa_causal_t16384_d128_sampled(fa):
     # B=2, Hq=32, Hkv=8, T=16384, d=128, causal, 1% of K rows x8: a kv head's gradient sums
     # four query heads.
-    sampled_e2e(fa, inputs.CONFIGS["c5_bf16_gqa_causal_t16384_d128"], [(1, 17)], [(0, 3)])
+    sampled_e2e(fa, inputs.CONFIGS["bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"], [(1, 17)], [(0, 3)])

@@ -131,13 +131,13 @@ def test_bitwise_equal_to_the_contiguous_decode(fa):
 def test_workload_gqa_decode_paged_full(fa):
     # The GQA decode workload (B=64, Hq=64, Hkv=8, 8192 cached positions, d=128) in 16-position
     # pages, every output against the oracle.
-    cfg = inputs.CONFIGS["c4_bf16_gqa_decode_tk8192_d128"]
+    cfg = inputs.CONFIGS["bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128"]
     _say("gqa decode paged: inputs")
     paged_case(fa, cfg, 16, [8192] * cfg.B)
 
 
 def test_workload_gqa_decode_paged_ragged(fa):
-    cfg = inputs.CONFIGS["c4_bf16_gqa_decode_tk8192_d128"].replace(B=16, name="c4 ragged")
+    cfg = inputs.CONFIGS["bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128"].replace(B=16, name="gqa decode ragged lengths")
     lens = np.random.default_rng(99).integers(1, 8193, size=16)
     lens[0], lens[1] = 8192, 1
     _say("gqa decode paged ragged")

@@ -170,7 +170,7 @@ def test_zero_queries_give_prefix_means(fa):
 
 
 def test_large_logit_spikes(fa):
-    # K rows scaled x8 (C5's stress) on a small problem, compared in full
+    # K rows scaled x8 (the spiked-key stress of the GQA T=16384 workload) on a small problem, compared in full
     cfg = AttnConfig("spikes", B=1, Hq=4, Hkv=1, Tq=700, Tk=700, d=128, dtype="bf16",
                      causal=True, dist="normal", seed=21, k_spike=(0.01, 8.0))
     full_case(fa, cfg)
@@ -265,30 +265,30 @@ def sampled_case(fa, cfg: AttnConfig, heads):
           np.concatenate(orf), np.concatenate(lrf), cfg.dtype, cfg.name)
 
 
-def test_c1_full(fa):
-    full_case(fa, inputs.CONFIGS["c1_f32_causal_t128_d32"])
+def test_f32_causal_t128_d32_full(fa):
+    full_case(fa, inputs.CONFIGS["f32_causal_b1_h4_t128_d32"])
 
 
-def test_c2_full(fa):
-    full_case(fa, inputs.CONFIGS["c2_bf16_causal_t1024_d64"])
+def test_bf16_causal_t1024_d64_full(fa):
+    full_case(fa, inputs.CONFIGS["bf16_causal_b4_h16_t1024_d64"])
 
 
-@pytest.mark.parametrize("name", ["c3_bf16_causal_t8192_d128", "c3_bf16_noncausal_t4096_d128",
-                                  "c3_bf16_causal_t8000_d128"])
-def test_c3_sampled(fa, name):
+@pytest.mark.parametrize("name", ["bf16_causal_b1_h32_t8192_d128", "bf16_noncausal_b1_h32_t4096_d128",
+                                  "bf16_causal_b1_h32_t8000_d128"])
+def test_bf16_t8192_shapes_sampled(fa, name):
     cfg = inputs.CONFIGS[name]
     sampled_case(fa, cfg, heads=[(0, 0), (0, 13), (0, 31)])
 
 
-def test_c3_ragged_noncausal_sampled(fa):
-    cfg = inputs.CONFIGS["c3_bf16_causal_t8000_d128"].replace(causal=False, name="c3 ragged nc")
+def test_bf16_noncausal_t8000_sampled(fa):
+    cfg = inputs.CONFIGS["bf16_causal_b1_h32_t8000_d128"].replace(causal=False, name="noncausal t8000")
     sampled_case(fa, cfg, heads=[(0, 5)])
 
 
-def test_c4_full(fa):
+def test_gqa_decode_full(fa):
     import torch
 
-    cfg = inputs.CONFIGS["c4_bf16_gqa_decode_tk8192_d128"]
+    cfg = inputs.CONFIGS["bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128"]
     _say(f"{cfg.name}: generating inputs")
     Q, K, V = inputs.make_inputs(cfg)
     o, l = run_gpu(fa, Q, K, V, cfg.causal, cfg.scale, cfg.dtype)
@@ -305,6 +305,6 @@ def test_c4_full(fa):
     check(o, l, o_ref, l_ref, cfg.dtype, cfg.name)
 
 
-def test_c5_sampled(fa):
-    cfg = inputs.CONFIGS["c5_bf16_gqa_causal_t16384_d128"]
+def test_gqa_causal_t16384_sampled(fa):
+    cfg = inputs.CONFIGS["bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"]
     sampled_case(fa, cfg, heads=[(0, 0), (0, 3), (1, 17), (1, 31)])

@@ -145,7 +145,7 @@ def _sample_rows(T, W, rng, n=24):
 def test_window_prefill_t8192_w4096_sampled(fa):
     import torch
 
-    cfg = inputs.CONFIGS["c3_bf16_causal_t8192_d128"]
+    cfg = inputs.CONFIGS["bf16_causal_b1_h32_t8192_d128"]
     W = 4096
     _say(f"{cfg.name} W={W}: inputs")
     Q, K, V = inputs.make_inputs(cfg)
@@ -168,7 +168,7 @@ def test_window_prefill_t8192_w4096_sampled(fa):
 
 
 def test_window_decode_gqa_tk8192_w4096_full(fa):
-    cfg = inputs.CONFIGS["c4_bf16_gqa_decode_tk8192_d128"]
+    cfg = inputs.CONFIGS["bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128"]
     W = 4096
     _say(f"{cfg.name} W={W}: inputs")
     Q, K, V = inputs.make_inputs(cfg)

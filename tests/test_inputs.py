@@ -20,7 +20,7 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_slices_are_reproducible_and_distinct():
-    cfg = inputs.CONFIGS["c2_bf16_causal_t1024_d64"]
+    cfg = inputs.CONFIGS["bf16_causal_b4_h16_t1024_d64"]
     a = inputs.head_slice(cfg, inputs.Q_ID, 1, 3)
     b = inputs.head_slice(cfg, inputs.Q_ID, 1, 3)
     c = inputs.head_slice(cfg, inputs.K_ID, 1, 3)
@@ -30,7 +30,7 @@ def test_slices_are_reproducible_and_distinct():
 
 
 def test_k_spikes():
-    cfg = inputs.CONFIGS["c5_bf16_gqa_causal_t16384_d128"].replace(Tq=1000, Tk=1000)
+    cfg = inputs.CONFIGS["bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"].replace(Tq=1000, Tk=1000)
     k = inputs.head_slice(cfg, inputs.K_ID, 0, 1)
     plain = inputs.head_slice(cfg.replace(k_spike=None), inputs.K_ID, 0, 1)
     changed = np.nonzero(np.any(k != plain, axis=1))[0]
