@@ -28,7 +28,9 @@
 //    only when a row's maximum exceeds it by more than kRebase (log2 units) are l and the
 //    accumulator rescaled. Any base gives the same O = acc / l and LSE = base + log l
 //    ("Efficient attention & KV cache", section 2.1: the max is there only for numerical
-//    safety); weights stay below 2^kRebase.
+//    safety); weights stay below 2^kRebase. For d <= 64 the steady state skips the row maximum
+//    altogether: it forms the weights against the current base and falls back to the maximum
+//    and a re-base only when a lane's sum of them (which bounds each one) exceeds 2^13.
 //  * the row sum adds the bf16 weights the PV product uses (v_dot2 against ones).
 #include <hip/hip_runtime.h>
 
@@ -57,6 +59,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     int causal, int window, float log2_scale, int qsign, int schedule,
     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
   using S = Shape<D, BC, NW>;
+  // d <= 64: the steady state takes no row maximum unless the weights could grow too large (the
+  // exponentials and the few other VALU instructions per score bound the step at these sizes;
+  // at d = 128 the scores kept live for the check would spill)
+  constexpr bool NOMAX = D <= 64;
   // One array per stage, so the compiler can tell a direct-to-LDS load into one stage from reads
   // of another and does not make those reads wait for the load.
   __shared__ __align__(1024) unsigned char k_st0[S::TILE], k_st1[S::TILE];
@@ -239,6 +245,27 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     }
   };
 
+  // weights of a score tile against the current base, with this lane's sum of them
+  auto weights_sum = [&](f32x16 (&s)[BC / 32], bf16x8 (&pb)[BC / 16]) {
+    const float base = (M == kNegInf) ? 0.f : M;
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+    float ts = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < BC / 16; ++ch) {
+      const int t = ch >> 1, c2 = ch & 1;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i], log2_scale, -base));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[t][8 * c2 + i + 1], log2_scale, -base));
+        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+        ts = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ts, false);
+        pb[ch][i] = pp[0];
+        pb[ch][i + 1] = pp[1];
+      }
+    }
+    return ts;
+  };
+
   // O^T += V^T P^T for one tile from a V stage
   auto pv = [&](const bf16x8 (&pb)[BC / 16], const unsigned char* vst) {
 #pragma unroll
@@ -292,9 +319,21 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     issue_tile(Kh, j0 + 2 * BC, k_cur);
     bf16x8 pb[BC / 16];
     qk(sn, k_nxt);
-    weights(sc, pb);
-    pv(pb, v_cur);
-    rebase(sn);
+    if constexpr (NOMAX) {
+      // weights against the current base; the row maximum only when a lane's weights could
+      // exceed 2^13 (their sum bounds each of them)
+      float ts = weights_sum(sc, pb);
+      if (__builtin_amdgcn_ballot_w64(!(ts <= 8192.f)) != 0) {
+        rebase(sc);
+        ts = weights_sum(sc, pb);
+      }
+      lsum += ts;
+      pv(pb, v_cur);
+    } else {
+      weights(sc, pb);
+      pv(pb, v_cur);
+      rebase(sn);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -331,6 +370,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   for (; j + 2 < jm; j += 2) {
     fast_step(sa, sb, j, k_st0, k_st1, v_st0, v_st1);
     fast_step(sb, sa, j + 1, k_st1, k_st0, v_st1, v_st0);
+  }
+  // the steady state leaves the scores of tile j without their maximum
+  if constexpr (NOMAX) {
+    if (j < ntiles && active(j)) rebase(sa);
   }
   for (; j < ntiles; ++j) general_step(j);
 

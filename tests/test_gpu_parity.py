@@ -169,11 +169,27 @@ def test_zero_queries_give_prefix_means(fa):
     check(o, l, expect, np.broadcast_to(np.log(cnt), l.shape), "bf16", "q=0 prefix means")
 
 
-def test_large_logit_spikes(fa):
-    # K rows scaled x8 (the spiked-key stress of the GQA T=16384 workload) on a small problem, compared in full
-    cfg = AttnConfig("spikes", B=1, Hq=4, Hkv=1, Tq=700, Tk=700, d=128, dtype="bf16",
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_large_logit_spikes(fa, d):
+    # 1% of the K rows scaled x8 (the spiked-key stress of the GQA T=16384 workload) on a small
+    # problem, compared in full
+    cfg = AttnConfig(f"spikes d{d}", B=1, Hq=4, Hkv=1, Tq=700, Tk=700, d=d, dtype="bf16",
                      causal=True, dist="normal", seed=21, k_spike=(0.01, 8.0))
     full_case(fa, cfg)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_scores_growing_along_the_keys(fa, d, causal):
+    # The keys' scale grows 16-fold along the sequence, so tile after tile exceeds the exponent
+    # base the rows have so far: the re-base paths of the steady state run again and again (for
+    # d <= 64 that is the fallback behind the weight-sum check).
+    cfg = _small(f"growing d{d} c{int(causal)}", 1, 4, 2, 900, 900, d, causal=causal, seed=d + 5)
+    Q, K, V = inputs.make_inputs(cfg)
+    K = inputs.round_to_bf16(K * np.linspace(0.25, 4.0, cfg.Tk)[None, None, :, None])
+    o, l = run_gpu(fa, Q, K, V, causal, cfg.scale, "bf16")
+    o_ref, l_ref = oracle.dense_attention(Q, K, V, causal, cfg.scale)
+    check(o, l, o_ref, l_ref, "bf16", cfg.name)
 
 
 def test_deterministic_and_no_out_of_bounds_writes(fa):
