@@ -26,7 +26,8 @@ struct Problem {
 };
 
 // bf16 matrix-core prefill. block_kv in {32, 64}, waves in {4, 8}, d in {32, 64, 128};
-// schedule 1 = row-major grid, 2 = XCD-grouped with the longest causal blocks first.
+// schedule 1 = row-major grid, 2 = whole heads per XCD, 8 heads at a time query-block-major with
+// the longest causal blocks first (grid_order.h).
 hipError_t launch_prefill_bf16(const Problem& p, int block_kv, int waves, int schedule,
                                hipStream_t stream);
 
@@ -41,8 +42,9 @@ struct Packed {
 
 // bf16 matrix-core prefill over a packed batch: p.B is the number of sequences, p.Tq and p.Tk
 // the longest lengths (the grid covers p.Tq rows per sequence; longer sequences are cut there),
-// LSE is [Hq, total_q]. block_kv, waves as for launch_prefill_bf16; schedule 3 is the
-// query-block-major order that balances sequences of different lengths.
+// LSE is [Hq, total_q]. block_kv, waves as for launch_prefill_bf16; schedule 3 deals the
+// (sequence, head) pairs to the XCDs by head, so every XCD gets a share of every sequence
+// (grid_order.h).
 hipError_t launch_prefill_varlen_bf16(const Problem& p, const Packed& pk, int block_kv,
                                       int waves, int schedule, hipStream_t stream);
 
