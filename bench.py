@@ -132,20 +132,21 @@ def probes(fa, torch):
     mfma_tflops = wgs * 8 * 32 * iters * 32768.0 / (min(t) * 1e-3) / 1e12
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-    rwgs = 8192
-    words = torch.empty(rwgs * 256, dtype=torch.int32, device="cuda")
+    rwgs = 16384
+    words = torch.empty(rwgs * 4, dtype=torch.int32, device="cuda")
 
     def read():
         rc = fa.lib.fattn_probe_hbm_read(buf.data_ptr(), nbytes, words.data_ptr(), rwgs, stream)
         assert rc == fa.FATTN_OK, rc
 
-    t = time_calls(torch, read, 3, 5)
+    t = time_calls(torch, read, 20, 10)
     read_gbs = nbytes / (min(t) * 1e-3) / 1e9
     del buf, words, out
     return {"mfma_bf16_tflops": round(mfma_tflops, 1), "hbm_read_gbs": round(read_gbs, 1),
-            "what": "best of 5 launches: 4 chains of v_mfma_f32_32x32x16_bf16 per wavefront on "
+            "what": "best of 5 (matrix) and 10 (read) launches: 4 chains of v_mfma_f32_32x32x16_bf16 per wavefront on "
                     "register operands (2048 x 8 wavefronts); 16-byte nontemporal loads over a "
-                    "4 GiB buffer (8192 x 256 threads)"}
+                    "4 GiB buffer, one contiguous 256 KiB chunk per workgroup (16384 x 256 "
+                    "threads)"}
 
 
 def source_hash(name):

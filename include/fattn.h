@@ -275,8 +275,9 @@ int fattn_release(void);
  * workgroups * 8 * 32 * iters * 32768.
  *
  * fattn_probe_hbm_read: enqueues `workgroups` workgroups of 256 threads that read the `bytes`
- * bytes at device pointer `buf` once with 16-byte nontemporal loads and write one word per
- * thread to `out` (at least workgroups * 256 words). `buf` must be 16-byte aligned and `bytes` a
+ * bytes at device pointer `buf` once with 16-byte nontemporal loads, workgroup w the w-th of
+ * `workgroups` equal contiguous chunks, and write one word per wavefront to `out` (at least
+ * workgroups * 4 words). `buf` must be 16-byte aligned and `bytes` a
  * positive multiple of 16.
  *
  * Both return FATTN_ERR_INVALID for a NULL pointer or a non-positive count (and, for the read

@@ -5,8 +5,8 @@
 //  * fattn_probe_mfma: every wavefront runs four independent chains of
 //    v_mfma_f32_32x32x16_bf16 (the prefill kernel's instruction) on register operands, eight
 //    wavefronts per workgroup; 32768 FLOPs per instruction.
-//  * fattn_probe_hbm_read: grid-stride 16-byte nontemporal loads over a buffer (the decode
-//    kernel's load form), one XOR-reduced word stored per thread.
+//  * fattn_probe_hbm_read: 16-byte nontemporal loads over a buffer (the decode kernel's load
+//    form), one contiguous chunk per workgroup, one XOR-reduced word stored per wavefront.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -45,18 +45,27 @@ __global__ __launch_bounds__(512) void probe_mfma_kernel(float* __restrict__ out
 
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ p, size_t n,
                                                          unsigned* __restrict__ out) {
+  // workgroup w reads the contiguous chunk [w * chunk, (w + 1) * chunk), eight loads in flight
+  // per thread (measured: about 7.1 TB/s with 8192-16384 workgroups over 4 GiB, against
+  // 6.3-6.8 for a grid-stride walk)
+  const size_t chunk = (n + gridDim.x - 1) / gridDim.x;
+  const size_t beg = (size_t)blockIdx.x * chunk;
+  const size_t end = beg + chunk < n ? beg + chunk : n;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 7 * stride < n; i += 8 * stride) {
+  size_t i = beg + threadIdx.x;
+  for (; i + 7 * 256 < end; i += 8 * 256) {
     u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + i + u * 256);
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u];
   }
-  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(p + i);
-  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  for (; i < end; i += 256) acc ^= __builtin_nontemporal_load(p + i);
+  // one word per wavefront (a word per thread added measurable write traffic at this grid size)
+  unsigned w = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) w ^= __shfl_xor(w, m);
+  if ((threadIdx.x & 63) == 0) out[(size_t)blockIdx.x * 4 + (threadIdx.x >> 6)] = w;
 }
 
 }  // namespace
