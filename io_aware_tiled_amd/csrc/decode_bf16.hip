@@ -12,9 +12,11 @@
 // section 2.1).
 //
 // Inside a chunk the G query heads that share a kv head form the 16-wide N side of
-// v_mfma_f32_16x16x32_bf16 (padded with zero rows when G < 16): S^T = K Q^T takes K straight
-// from global memory in the operand layout, and O^T = V^T P^T reads V^T from a small per-wave
-// LDS transpose whose key order matches the S^T accumulator, as in the prefill kernel.
+// v_mfma_f32_16x16x32_bf16 (padded with zero rows when G < 16): S^T = K Q^T reads K from a
+// per-wave LDS copy of the block (loaded from global memory as whole rows, 1 KB per load
+// instruction: reading the operand layout straight from memory, 16 rows a quarter each, streamed
+// about 10% slower), and O^T = V^T P^T reads V^T from a small per-wave LDS transpose whose key
+// order matches the S^T accumulator, as in the prefill kernel.
 //
 // The same kernels serve a paged cache ("Efficient attention & KV cache", section 2.5 and the
 // interview question on what PagedAttention changes in the kernel): keys and values sit in
@@ -44,9 +46,12 @@ __device__ __forceinline__ uint32_t pick_half(uint32_t a, uint32_t b, int hi) {
 
 template <int D>
 struct Block {
-  u32x4 k[2][D / 32];  // K rows kb+16t+lane%16, dims 32c + 8*(lane/16) .. +8
+  // K of half t: load c covers rows 16t + c*RPI .. +RPI-1 whole (RPI = 512 / D rows of D/8
+  // 16-byte chunks each), lane -> row c*RPI + lane/(D/8), chunk lane%(D/8)
+  u32x4 k[2][D / 32];
   u32x4 v[8];          // V rows of keys 4gg+r and 16+4gg+r, dims 8dg .. 8dg+8
 };
+constexpr int kPad = 8;  // LDS row pitch of K: D + 8 elements (16 bytes apart in the banks)
 
 // Where the 16-key halves of a 32-key block live. Keys kb + 16h + r (r < 16) are rows
 // row[h] + r of the K and V bases; a half whose rows are not readable has ok[h] false.
@@ -65,16 +70,18 @@ struct Halves {
 template <int D>
 __device__ __forceinline__ void load_block(Block<D>& blk, const __bf16* Kb, const __bf16* Vb,
                                            const Halves& hv, int kb, int kend, int lane) {
-  const int c16 = lane & 15, g4 = lane >> 4;
+  // K: each load reads whole rows (64 lanes x 16 bytes contiguous), which streams faster than
+  // reading 16 rows a quarter each in the operand layout; the rows go through LDS (kt_store)
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int key = kb + 16 * t + c16;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
+      const int r = c * RPI + lane / CPR;
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < kend && hv.ok[t])
+      if (kb + 16 * t + r < kend && hv.ok[t])
         x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            Kb + (hv.row[t] + c16) * D + 32 * c + 8 * g4));
+            Kb + (hv.row[t] + r) * D + 8 * (lane % CPR)));
       blk.k[t][c] = x;
     }
   }
@@ -131,6 +138,7 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
     int splits, int chunk, float log2_scale, int qsign, const int* __restrict__ table,
     const int* __restrict__ seq_lens, int max_blocks, int bs_shift, int nblocks) {
   __shared__ __align__(16) __bf16 Vt[D * VS];
+  __shared__ __align__(16) __bf16 Kt[KB * (D + kPad)];
 
   const int lane = threadIdx.x;
   const int c16 = lane & 15, g4 = lane >> 4;
@@ -201,15 +209,28 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
       }
     }
 
+    {
+      constexpr int CPR = D / 8, RPI = 64 / CPR;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+          *reinterpret_cast<u32x4*>(Kt + (16 * t + c * RPI + lane / CPR) * (D + kPad) +
+                                    8 * (lane % CPR)) = cur.k[t][c];
+    }
+    __syncthreads();  // K rows of this block are in LDS
+
     // S^T: rows = keys kb + 16t + 4*g4 + r, column = query qi
     f32x4 st[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       st[t] = f32x4{};
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[t][c]),
-                                                       qb[c], st[t], 0, 0, 0);
+      for (int c = 0; c < D / 32; ++c) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + (16 * t + c16) * (D + kPad) +
+                                                          32 * c + 8 * g4);
+        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[c], st[t], 0, 0, 0);
+      }
     }
     if (kb + KB > kend) {
 #pragma unroll
