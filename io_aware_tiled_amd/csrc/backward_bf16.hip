@@ -132,10 +132,10 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   const int nqb = (Tq + S::BR - 1) / S::BR;
   // Dense batches: each XCD a contiguous range of whole heads, 4 heads at a time block-major
   // (blocks of one size dispatched together). Packed batches, whose sequences differ in length:
-  // pairs dealt to the XCDs by head, each pair's blocks together.
+  // pairs dealt to the XCDs by head, 4 at a time block-major.
   int bh, qb;
   if (VARLEN) {
-    xcd_grouped_pairs<1>(blockIdx.x, gridDim.x / nqb, nqb, bh, qb);
+    xcd_grouped_pairs<4>(blockIdx.x, gridDim.x / nqb, nqb, bh, qb);
   } else {
     xcd_pair_groups<4>(blockIdx.x, gridDim.x, nqb, bh, qb);
   }
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   // grid order as in the dQ kernel; key blocks ascending: longest causal blocks first
   int bg, kb;
   if (VARLEN) {
-    xcd_grouped_pairs<1>(blockIdx.x, gridDim.x / nkb, nkb, bg, kb);
+    xcd_grouped_pairs<4>(blockIdx.x, gridDim.x / nkb, nkb, bg, kb);
   } else {
     xcd_pair_groups<4>(blockIdx.x, gridDim.x, nkb, bg, kb);
   }
