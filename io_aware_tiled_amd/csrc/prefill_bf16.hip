@@ -382,22 +382,55 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   float l_lo, l_hi;
   halves(lsum, l_lo, l_hi);
   const float l = l_lo + l_hi;
-  if (qrow >= Tq) return;
   // a packed sequence can have rows that see no key (causal, fewer keys than queries, or none):
   // O = 0 and LSE = -inf for them
   const bool empty = VARLEN && !(l > 0.f);
   const float inv = empty ? 0.f : 1.f / l;
-  __bf16* Orow = VARLEN ? O + ((size_t)(q_begin + qrow) * Hq + h) * D
-                        : O + (((size_t)b * Hq + h) * (size_t)Tq + qrow) * D;
+  // O goes out row-major through the wave's share of the (now idle) K/V stages: each store
+  // instruction writes whole rows (1 KB, contiguous for dense O), instead of 8-byte pieces of 32
+  // different rows. Measured: causal T = 8192 +1.3%, T = 1024 +7%.
+  constexpr int WAVE_BYTES = 32 * S::RB;
+  constexpr int PER_ARR = S::TILE / WAVE_BYTES;
+  if constexpr (PER_ARR >= 1 && NW <= 4 * PER_ARR) {
+    constexpr int C = D / 8;  // 16-byte chunks per row; chunk c of row r sits at c ^ (r % C)
+    const int arr = wave / PER_ARR;
+    unsigned char* ob = (arr == 0 ? k_st0 : arr == 1 ? k_st1 : arr == 2 ? v_st0 : v_st1) +
+                        (wave % PER_ARR) * WAVE_BYTES;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = 32 * dt + 8 * g4 + 4 * hf;
-      u32x2 packed = {pack2_bf16(acc[dt][4 * g4 + 0] * inv, acc[dt][4 * g4 + 1] * inv),
-                      pack2_bf16(acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv)};
-      *reinterpret_cast<u32x2*>(Orow + d0) = packed;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = 4 * dt + g4;
+        u32x2 packed = {pack2_bf16(acc[dt][4 * g4 + 0] * inv, acc[dt][4 * g4 + 1] * inv),
+                        pack2_bf16(acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv)};
+        *(LDS_AS u32x2*)(ob + col * S::RB + ((c ^ (col % C)) << 4) + 8 * hf) = packed;
+      }
+    // the wave's own LDS operations run in order: only the compiler must not move the reads up
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // row qw0 + r of this head: packed batches keep Hq * D elements between rows
+    __bf16* Ow = VARLEN ? O + ((size_t)(q_begin + qw0) * Hq + h) * D
+                        : O + (((size_t)b * Hq + h) * (size_t)Tq + qw0) * D;
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i) {
+      const int r = i * (64 / C) + lane / C, lc = lane % C;
+      const u32x4 v = *(LDS_AS u32x4*)(ob + r * S::RB + ((lc ^ (r % C)) << 4));
+      if (qw0 + r < Tq) *reinterpret_cast<u32x4*>(Ow + (size_t)r * qstr + 8 * lc) = v;
     }
+    if (qrow >= Tq) return;
+  } else {
+    if (qrow >= Tq) return;
+    __bf16* Orow = VARLEN ? O + ((size_t)(q_begin + qrow) * Hq + h) * D
+                          : O + (((size_t)b * Hq + h) * (size_t)Tq + qrow) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hf;
+        u32x2 packed = {pack2_bf16(acc[dt][4 * g4 + 0] * inv, acc[dt][4 * g4 + 1] * inv),
+                        pack2_bf16(acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv)};
+        *reinterpret_cast<u32x2*>(Orow + d0) = packed;
+      }
+  }
   if (hf == 0) {
     const float lse = empty ? kNegInf : (M + __builtin_amdgcn_logf(l)) * kLn2;
     if constexpr (VARLEN)
