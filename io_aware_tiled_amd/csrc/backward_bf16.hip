@@ -109,6 +109,51 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict_
   }
 }
 
+// A wave's 32 gradient rows (lane (col, hf) holds dims 32dt + 8g4 + 4hf .. +3 of row col in
+// acc[dt][4g4 .. 4g4+3], the MFMA accumulator layout), times `mul`, rounded to bf16 and stored as
+// whole rows: 16 rows at a time through the wave's 16-row share of four idle LDS stage arrays,
+// 16-byte chunks XOR-swizzled by row, then one row-contiguous chunk per lane per store (instead
+// of 8-byte pieces of 32 rows per instruction). Rows r < nvalid go to base + r * stride.
+// Every wave of the workgroup must call it (it starts with a barrier: the stages are free).
+template <int D, int BC, int NW>
+__device__ __forceinline__ void store_rows(unsigned char* a0, unsigned char* a1,
+                                           unsigned char* a2, unsigned char* a3, int wave,
+                                           int lane, const f32x16 (&acc)[D / 32], float mul,
+                                           __bf16* base, size_t stride, int nvalid) {
+  using S = Shape<D, BC, NW>;
+  constexpr int C = D / 8, HALF = 16 * S::RB, PER = S::TILE / HALF;
+  static_assert(PER >= 1 && NW <= 4 * PER, "stage arrays too small for the row staging");
+  const int col = lane & 31, hf = lane >> 5;
+  const int arr = wave / PER;
+  unsigned char* ob = (arr == 0 ? a0 : arr == 1 ? a1 : arr == 2 ? a2 : a3) + (wave % PER) * HALF;
+  __syncthreads();
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((col >> 4) == half) {
+      const int r = col & 15;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int c = 4 * dt + g4;
+          u32x2 packed = {pack2_bf16(acc[dt][4 * g4 + 0] * mul, acc[dt][4 * g4 + 1] * mul),
+                          pack2_bf16(acc[dt][4 * g4 + 2] * mul, acc[dt][4 * g4 + 3] * mul)};
+          *(LDS_AS u32x2*)(ob + r * S::RB + ((c ^ (r % C)) << 4) + 8 * hf) = packed;
+        }
+    }
+    // the wave's own LDS operations run in order: only the compiler must keep this order
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int i = 0; i < C / 4; ++i) {
+      const int r = i * (64 / C) + lane / C, lc = lane % C;
+      const u32x4 v = *(LDS_AS u32x4*)(ob + r * S::RB + ((lc ^ (r % C)) << 4));
+      const int row = 16 * half + r;
+      if (row < nvalid) *reinterpret_cast<u32x4*>(base + (size_t)row * stride + 8 * lc) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
+}
+
 // ---- dQ: one workgroup per (batch, query head, block of 32 * NW query rows).
 // VARLEN: packed batch (Q, dO, dQ [total_q, Hq, D], K, V [total_k, Hkv, D], the workspace of
 // bwd_prep_packed_kernel); blockIdx covers (sequence, head, query block) with Tq and Tk the
@@ -330,18 +375,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
   }
   if (j < ntiles) step(j, k_st0, v_st0, k_st1, v_st1);
 
-  if (qrow >= Tq) return;
-  __bf16* row = VARLEN ? dQ + ((size_t)(q_begin + qrow) * Hq + h) * D
-                       : dQ + ((size_t)bh * Tq + qrow) * D;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = 32 * dt + 8 * g4 + 4 * hf;
-      u32x2 packed = {pack2_bf16(acc[dt][4 * g4 + 0] * scale, acc[dt][4 * g4 + 1] * scale),
-                      pack2_bf16(acc[dt][4 * g4 + 2] * scale, acc[dt][4 * g4 + 3] * scale)};
-      *reinterpret_cast<u32x2*>(row + d0) = packed;
-    }
+  // rows qw0 .. qw0+31 of this head (packed batches keep Hq * D elements between rows)
+  __bf16* rows = VARLEN ? dQ + ((size_t)(q_begin + qw0) * Hq + h) * D
+                        : dQ + ((size_t)bh * Tq + qw0) * D;
+  store_rows<D, BC, NW>(k_st0, k_st1, v_st0, v_st1, wave, lane, acc, scale, rows,
+                        VARLEN ? (size_t)Hq * D : (size_t)D, Tq - qw0);
 }
 
 // ---- dK, dV: one workgroup per (batch, kv head, block of 32 * NW keys); the loop runs over the
@@ -585,23 +623,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   }
   if (s < nsteps) step(s, q_st0, o_st0, lw_st0, q_st1, o_st1, lw_st1);
 
-  if (kcol >= Tk) return;
-  __bf16* krow = VARLEN ? dK + ((size_t)(k_begin + kcol) * Hkv + g) * D
-                        : dK + ((size_t)bg * Tk + kcol) * D;
-  __bf16* vrow = VARLEN ? dV + ((size_t)(k_begin + kcol) * Hkv + g) * D
-                        : dV + ((size_t)bg * Tk + kcol) * D;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d0 = 32 * dt + 8 * g4 + 4 * hf;
-      u32x2 pk = {pack2_bf16(dk[dt][4 * g4 + 0] * scale, dk[dt][4 * g4 + 1] * scale),
-                  pack2_bf16(dk[dt][4 * g4 + 2] * scale, dk[dt][4 * g4 + 3] * scale)};
-      u32x2 pv = {pack2_bf16(dv[dt][4 * g4 + 0], dv[dt][4 * g4 + 1]),
-                  pack2_bf16(dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3])};
-      *reinterpret_cast<u32x2*>(krow + d0) = pk;
-      *reinterpret_cast<u32x2*>(vrow + d0) = pv;
-    }
+  // keys kw0 .. kw0+31 of this kv head (packed batches keep Hkv * D elements between rows)
+  const size_t kstride = VARLEN ? (size_t)Hkv * D : (size_t)D;
+  const size_t k_off = VARLEN ? ((size_t)(k_begin + kw0) * Hkv + g) * D : ((size_t)bg * Tk + kw0) * D;
+  store_rows<D, BC, NW>(q_st0, q_st1, o_st0, o_st1, wave, lane, dk, scale, dK + k_off, kstride,
+                        Tk - kw0);
+  store_rows<D, BC, NW>(q_st0, q_st1, o_st0, o_st1, wave, lane, dv, 1.f, dV + k_off, kstride,
+                        Tk - kw0);
 }
 
 // dQ and dK/dV launches with DQ_NW waves per dQ workgroup (32 * DQ_NW query rows) and KV_NW
