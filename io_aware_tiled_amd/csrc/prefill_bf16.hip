@@ -183,7 +183,22 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     }
   };
 
+  // d = 128: key j0 + 4*hf + k of element (t, r) has k = 32t + 8(r/4) + r%4, a constant; the
+  // bounds move into this lane's frame once, and without a window only the upper one is tested
+  // (0.5% on causal shapes; at d <= 64 the two versions cost registers and occupancy)
   auto mask_tile = [&](f32x16 (&s)[BC / 32], int j0) {
+    if constexpr (D == 128) {
+      const int base = j0 + 4 * hf;
+      const int hi = (causal ? min(Tk - 1, qrow + off) : Tk - 1) - base;
+      if (window == 0) {
+#pragma unroll
+        for (int t = 0; t < BC / 32; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * t + 8 * (r >> 2) + (r & 3) > hi) s[t][r] = kNegInf;
+        return;
+      }
+    }
     const int last = causal ? min(Tk - 1, qrow + off) : Tk - 1;
     const int first = window > 0 ? qrow + off - window + 1 : 0;
 #pragma unroll
