@@ -88,7 +88,8 @@ int make_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dty
       if (dtype != FATTN_BF16) return FATTN_ERR_UNSUPPORTED;
       const PrefillEntry* e = nullptr;
       for (const PrefillEntry& r : kPrefillTable) {
-        if (r.d == d && (r.causal < 0 || r.causal == causal) && (r.tk_max == 0 || Tk <= r.tk_max)) {
+        if (r.d == d && (r.causal < 0 || r.causal == causal) && (r.tk_max == 0 || Tk <= r.tk_max) &&
+            (long long)B * Hq >= r.min_bh) {
           e = &r;
           break;
         }

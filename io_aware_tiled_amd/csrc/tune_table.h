@@ -7,7 +7,8 @@
 // parity tests run each one.
 //
 // Prefill rows are matched in order: the first row whose d matches, whose causal flag matches
-// (-1 = either) and whose Tk is at most tk_max (0 = no bound) wins.
+// (-1 = either), whose Tk is at most tk_max (0 = no bound) and whose batch x query heads is at
+// least min_bh wins.
 #pragma once
 
 namespace fattn {
@@ -16,6 +17,7 @@ struct PrefillEntry {
   int d;
   int causal;   // -1 = any
   int tk_max;   // 0 = unbounded
+  int min_bh;   // B * Hq at least this (0 = any)
   int block_kv;
   int waves;
   int schedule;
@@ -27,24 +29,26 @@ struct PrefillEntry {
 //    633 vs 541 with 8 waves; B = 16, T = 1024: 635 vs 604), 8 waves beyond (B = 1, T = 4096:
 //    966 vs 913; T = 8192: 1108 vs 1074).
 //  * d = 128, no mask: 4 waves up to Tk = 1024 (887 vs 860), 8 waves beyond.
-//  * d = 64, causal: 64-key tiles with 4 waves up to Tk = 1024 (B = 4, H = 16: 302 vs 296),
-//    32-key tiles with 4 waves beyond (T = 2048 to 16384 with 32 heads: 2-3% faster, e.g.
-//    T = 8192: 940 vs 922).
+//  * d = 64, causal: up to Tk = 1024, 32-key tiles with 4 waves for at least 256 (batch, head)
+//    pairs (B = 16, H = 32: 637 vs 606 with 64-key tiles), 64-key tiles with 4 waves for fewer
+//    (B = 4, H = 16: 326 vs 316); 32-key tiles with 4 waves beyond (T = 2048 to 16384 with 32
+//    heads: 2-3% faster, e.g. T = 8192: 946 vs 932).
 //  * d = 64, no mask: 32-key tiles with 4 waves up to Tk = 1024, with 8 waves beyond
 //    (T = 2048: 932 vs 908; T = 8192: 1008 vs 975).
 // 64-key tiles win everywhere else; the XCD-grouped, longest-first order is 1.3-1.5x faster
 // than row-major for causal masks and no slower without one.
 static const PrefillEntry kPrefillTable[] = {
-    // d, causal, tk_max, block_kv, waves, schedule
-    {128, 1, 2048, 64, 4, 2},
-    {128, 1, 0, 64, 8, 2},
-    {128, 0, 1024, 64, 4, 2},
-    {128, 0, 0, 64, 8, 2},
-    {64, 1, 1024, 64, 4, 2},
-    {64, 1, 0, 32, 4, 2},
-    {64, 0, 1024, 32, 4, 2},
-    {64, 0, 0, 32, 8, 2},
-    {32, -1, 0, 64, 4, 2},
+    // d, causal, tk_max, min_bh, block_kv, waves, schedule
+    {128, 1, 2048, 0, 64, 4, 2},
+    {128, 1, 0, 0, 64, 8, 2},
+    {128, 0, 1024, 0, 64, 4, 2},
+    {128, 0, 0, 0, 64, 8, 2},
+    {64, 1, 1024, 256, 32, 4, 2},
+    {64, 1, 1024, 0, 64, 4, 2},
+    {64, 1, 0, 0, 32, 4, 2},
+    {64, 0, 1024, 0, 32, 4, 2},
+    {64, 0, 0, 0, 32, 8, 2},
+    {32, -1, 0, 0, 64, 4, 2},
 };
 
 // Decode: number of workgroups to aim for across the whole grid and the smallest key chunk a
