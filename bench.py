@@ -328,7 +328,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "this build has no multi-GPU path; shard (batch, kv-head) groups across GPUs "
+              "libfattn has no multi-GPU path; shard (batch, kv-head) groups across GPUs "
               "with one process each instead.", file=sys.stderr)
         sys.exit(2)
 
