@@ -307,14 +307,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
   // ---- prologue: clear the V stages (rows past Tk must never hold non-finite leftovers), then
   // load K(j_lo), V(j_lo), K(j_lo+1); scores, mask and maximum of tile j_lo. Stages alternate
   // with j - j_lo.
-  for (int i = tid; i < S::TILE / 16; i += S::NT) {
-    *(LDS_AS u32x4*)(v_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-    *(LDS_AS u32x4*)(v_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  // (with Tk a multiple of BC every row a PV product reads is loaded, and the clear is skipped)
+  if (Tk % BC != 0) {
+    for (int i = tid; i < S::TILE / 16; i += S::NT) {
+      *(LDS_AS u32x4*)(v_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+      *(LDS_AS u32x4*)(v_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
   }
-  __syncthreads();
   issue_tile(Kh, j_lo * BC, k_st0);
   issue_tile(Vh, j_lo * BC, v_st0);
-  issue_tile(Kh, (j_lo + 1) * BC, k_st1);
+  if (j_lo + 1 < ntiles) issue_tile(Kh, (j_lo + 1) * BC, k_st1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   f32x16 sa[BC / 32], sb[BC / 32];
@@ -360,8 +363,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     unsigned char* k_nxt = odd ? k_st0 : k_st1;
     unsigned char* v_cur = odd ? v_st1 : v_st0;
     unsigned char* v_nxt = odd ? v_st0 : v_st1;
-    issue_tile(Vh, j0 + BC, v_nxt);
-    issue_tile(Kh, j0 + 2 * BC, k_cur);
+    // no loads of tiles past the last one: the step's closing wait would wait for them
+    if (j + 1 < ntiles) issue_tile(Vh, j0 + BC, v_nxt);
+    if (j + 2 < ntiles) issue_tile(Kh, j0 + 2 * BC, k_cur);
     const bool act_next = (j + 1 < ntiles) && active(j + 1);
     if (act_next) {
       qk(sb, k_nxt);
