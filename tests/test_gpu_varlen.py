@@ -75,6 +75,14 @@ def test_length_mix(fa, d, causal):
     varlen_case(fa, _cfg(4, 2, d, seed=d, causal=causal), MIX)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("d", [64, 128])
+def test_whole_tile_lengths(fa, d, causal):
+    # every document a multiple of the key tile: no tile has rows past its document's end, the
+    # case where the kernels skip clearing their value stages
+    varlen_case(fa, _cfg(4, 2, d, seed=d + 3, causal=causal), [64, 128, 256, 32, 512])
+
+
 def test_more_keys_than_queries(fa):
     varlen_case(fa, _cfg(4, 2, 128), [5, 100, 64, 1], [40, 300, 64, 129])
 
