@@ -73,3 +73,19 @@ def test_decode_bytes_of_gqa_step():
     b = acc.decode_bytes(64, 64, 8, 8192, 128)
     assert b == 2 * 64 * 8 * 8192 * 128 * 2 + 2 * 64 * 64 * 128 * 2 + 4 * 64 * 64
     assert round(b / 1e9, 4) == 2.1496
+
+
+def test_prefill_compulsory_bytes():
+    # B=1, H=32, T=8192, d=128 bf16: Q, K, V read once and O written (4 x 64 MiB) plus the fp32
+    # LSE (1 MiB) = 269.48 MB. Under GQA only K and V shrink with the kv head count, and the
+    # byte count is linear in the element size except for the fp32 LSE.
+    assert acc.prefill_compulsory_bytes(1, 32, 32, 8192, 8192, 128) == 4 * 2**26 + 2**20
+    full = acc.prefill_compulsory_bytes(2, 32, 32, 4096, 4096, 128)
+    gqa = acc.prefill_compulsory_bytes(2, 32, 8, 4096, 4096, 128)
+    kv_mha = 2 * 2 * 32 * 4096 * 128 * 2
+    assert full - gqa == kv_mha - kv_mha // 4
+    lse = 4 * 2 * 32 * 4096
+    assert acc.prefill_compulsory_bytes(2, 32, 8, 4096, 4096, 128, dtype_bytes=4) - lse == \
+        2 * (gqa - lse)
+    # the attention_bytes model (Q, K, V, O of equal length, MHA) agrees without the LSE
+    assert acc.attention_bytes(2, 32, 4096, 128) == full - lse
