@@ -15,10 +15,12 @@
 //    streams the K and V tiles of its head; per tile S^T and dP^T come from two MFMA products
 //    against Q^T and dO^T held in registers, dS is formed on the VALU, and dQ^T += K^T dS^T
 //    reads the same K tile transposed.
-//  * bwd_dkdv_kernel (key-block outer loop): a lane owns a key and holds K^T and V^T in
-//    registers; it streams the Q, dO and (L, D) tiles of every query head of its group, forms S
-//    and dP, then dV^T += dO^T P and dK^T += Q^T dS. dK and dV of a key are accumulated in
-//    registers over all the query heads that share it, so GQA needs no reduction pass.
+//  * bwd_dkdv_kernel (key-block outer loop): a lane owns a key and holds V^T in registers; the
+//    workgroup's K rows sit in LDS for its whole life (read as the K^T operand), which keeps the
+//    kernel within 256 registers and so at two waves per SIMD. It streams the Q, dO and (L, D)
+//    tiles of every query head of its group, forms S and dP, then dV^T += dO^T P and
+//    dK^T += Q^T dS. dK and dV of a key are accumulated in registers over all the query heads
+//    that share it, so GQA needs no reduction pass.
 // The split recomputes S and dP once per kernel (7 products instead of 5) in exchange for no
 // atomic accumulation of dQ: the first page above notes that the usual key-outer order adds dQ
 // with atomics and is therefore not reproducible run to run, and that a deterministic mode pays
@@ -386,7 +388,10 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
 // query heads of the group and, in each, over the query tiles of BC rows that see a key of the
 // block.
 // VARLEN: packed batch, as for the dQ kernel; blockIdx covers (sequence, kv head, key block).
-template <int D, int BC, int NW, int MINW, bool VARLEN>
+// KLDS: the workgroup's K rows live in LDS and are read as the K^T operand of every tile, instead
+// of K^T in registers. At d = 128 this frees the 32 registers that bring the kernel within 256,
+// so two waves run per SIMD instead of one.
+template <int D, int BC, int NW, int MINW, bool KLDS, bool VARLEN>
 __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dK,
@@ -400,6 +405,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   __shared__ __align__(1024) unsigned char q_st0[S::TILE], q_st1[S::TILE];
   __shared__ __align__(1024) unsigned char o_st0[S::TILE], o_st1[S::TILE];
   __shared__ __align__(16) float lw_st0[64 * LWB], lw_st1[64 * LWB];
+  __shared__ __align__(1024) unsigned char k_blk[KLDS ? NW * S::TILE : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -440,17 +446,20 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   const __bf16* Kh = VARLEN ? K + ((size_t)k_begin * Hkv + g) * D : K + (size_t)bg * Tk * D;
   const __bf16* Vh = VARLEN ? V + ((size_t)k_begin * Hkv + g) * D : V + (size_t)bg * Tk * D;
 
-  // ---- this lane's key: K^T and V^T operands
-  bf16x8 kb8[D / 16], vb8[D / 16];
+  // ---- this lane's key: the V^T operand, and K^T unless the K block is loaded into LDS below
+  bf16x8 kb8[KLDS ? 1 : D / 16], vb8[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
-    if (kcol < Tk) {
-      rk = *reinterpret_cast<const u32x4*>(Kh + (size_t)kcol * kstr + 16 * kk + 8 * hf);
+    u32x4 rv = {0u, 0u, 0u, 0u};
+    if (kcol < Tk)
       rv = *reinterpret_cast<const u32x4*>(Vh + (size_t)kcol * kstr + 16 * kk + 8 * hf);
-    }
-    kb8[kk] = __builtin_bit_cast(bf16x8, rk);
     vb8[kk] = __builtin_bit_cast(bf16x8, rv);
+    if constexpr (!KLDS) {
+      u32x4 rk = {0u, 0u, 0u, 0u};
+      if (kcol < Tk)
+        rk = *reinterpret_cast<const u32x4*>(Kh + (size_t)kcol * kstr + 16 * kk + 8 * hf);
+      kb8[kk] = __builtin_bit_cast(bf16x8, rk);
+    }
   }
 
   // ---- query rows that see a key of this block: causal rows from k0 - off on; under a window
@@ -468,6 +477,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
     const int q = wave + i * NW;
     const int r = q * S::RPI + lane / S::C;
     dvo[i] = r * qrb + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
+  }
+  int dvk[S::NI_W];
+#pragma unroll
+  for (int i = 0; i < S::NI_W; ++i) {
+    const int q = wave + i * NW;
+    const int r = q * S::RPI + lane / S::C;
+    dvk[i] = r * (VARLEN ? (int)(kstr * 2) : S::RB) + (((lane % S::C) ^ swz<D, BC, NW>(r)) << 4);
   }
   const int ka = rowbase<D, BC, NW>(col) ^ (hf << 4);
   const int vq = lane >> 5, vg = (lane >> 4) & 1, ve = (lane >> 2) & 3, va = lane & 3;
@@ -528,6 +544,20 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
       }
     }
   };
+  // tile rows (queries) x this lane's key, against this wave's K tile in LDS
+  auto rows_xk = [&](f32x16 (&s)[BC / 32], const unsigned char* st) {
+    const unsigned char* kst = k_blk + wave * S::TILE;
+#pragma unroll
+    for (int t = 0; t < BC / 32; ++t) {
+      s[t] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 a = *(const LDS_AS bf16x8*)(st + ((ka ^ (kk << 5)) + 32 * t * S::RB));
+        const bf16x8 bk = *(const LDS_AS bf16x8*)(kst + (ka ^ (kk << 5)));
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bk, s[t], 0, 0, 0);
+      }
+    }
+  };
   // acc^T += tile^T x (bf16 operand whose k index runs over the tile rows)
   auto tr_x = [&](f32x16 (&a)[D / 32], const bf16x8 (&pb)[BC / 16], const unsigned char* st) {
 #pragma unroll
@@ -552,7 +582,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
     const bool masked = q0 + BC > Tq || (causal && q0 + off < kw0 + 31) ||
                         (window > 0 && q0 + BC - 1 + off - window + 1 > kw0);
     f32x16 sc[BC / 32], dp[BC / 32];
-    rows_x(sc, qst, kb8);
+    if constexpr (KLDS) {
+      rows_xk(sc, qst);
+    } else {
+      rows_x(sc, qst, kb8);
+    }
     rows_x(dp, ost, vb8);
     bf16x8 pb[BC / 16], db[BC / 16];
     // visible rows of the tile for this lane's key (relative to q0); empty when row_hi < row_lo
@@ -605,6 +639,14 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
     *(LDS_AS u32x4*)(o_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
+#pragma unroll
+  for (int w = 0; w < (KLDS ? NW : 0); ++w) {
+    if constexpr (VARLEN) {
+      dma_tile_strided<D, BC, NW>(Kh, k0 + 32 * w, Tk, (int)kstr, k_blk + w * S::TILE, wave, dvk);
+    } else {
+      dma_tile<D, BC, NW>(Kh, k0 + 32 * w, Tk, k_blk + w * S::TILE, wave, dvk);
+    }
+  }
   if (nsteps > 0) issue(0, q_st0, o_st0, lw_st0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -656,15 +698,18 @@ hipError_t launch_grads(const BwdProblem& p, const Packed* pk, float* ws, float 
         Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
         p.window, p.scale, c, nullptr, nullptr, 0, 0);
 
-  constexpr int KV_BC = 32, KV_MINW = D >= 128 ? 1 : 2;
+  // K in LDS for the 8-wave dK/dV workgroups at d = 128 (two waves per SIMD); elsewhere K^T in
+  // registers (one wave per SIMD at d = 128, two below)
+  constexpr bool KLDS = D >= 128 && KV_NW == 8;
+  constexpr int KV_BC = 32, KV_MINW = (KLDS || D < 128) ? 2 : 1;
   const int nkb = (p.Tk + 32 * KV_NW - 1) / (32 * KV_NW);
   const dim3 kv_grid((unsigned)(p.B * p.Hkv * nkb)), kv_block(64 * KV_NW);
   if (pk)
-    bwd_dkdv_kernel<D, KV_BC, KV_NW, KV_MINW, true><<<kv_grid, kv_block, 0, stream>>>(
+    bwd_dkdv_kernel<D, KV_BC, KV_NW, KV_MINW, KLDS, true><<<kv_grid, kv_block, 0, stream>>>(
         Q, K, V, dO, ws, static_cast<__bf16*>(p.dK), static_cast<__bf16*>(p.dV), p.Hq, p.Hkv,
         p.Tq, p.Tk, p.causal, p.window, p.scale, c, cu_q, cu_k, total_q, total_k);
   else
-    bwd_dkdv_kernel<D, KV_BC, KV_NW, KV_MINW, false><<<kv_grid, kv_block, 0, stream>>>(
+    bwd_dkdv_kernel<D, KV_BC, KV_NW, KV_MINW, KLDS, false><<<kv_grid, kv_block, 0, stream>>>(
         Q, K, V, dO, ws, static_cast<__bf16*>(p.dK), static_cast<__bf16*>(p.dV), p.Hq, p.Hkv,
         p.Tq, p.Tk, p.causal, p.window, p.scale, c, nullptr, nullptr, 0, 0);
   return hipGetLastError();
@@ -694,13 +739,19 @@ hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_
   // most the window). Up to 2048: 4-wave dQ workgroups (128 query rows) and 2-wave dK/dV
   // workgroups (64 keys), whose doubled workgroup count balances the CUs better, against 8 and
   // 4 waves 16-21% faster on causal d = 64 and 128 at T = 1024 and 2048 and 5% on a packed
-  // batch of 35 documents up to 4096 tokens. Beyond, 8 and 4 waves, which read Q and dO (K and
-  // V) half as often per key (query row): 3% faster on non-causal d = 128 from T = 4096 on and
-  // on a packed batch of 8 documents up to 8192 tokens, equal on causal T = 8192.
+  // batch of 35 documents up to 4096 tokens. Beyond, 8-wave dQ workgroups, which read K and V
+  // half as often per query row, and 8-wave dK/dV workgroups with the K block in LDS at d = 128
+  // (one workgroup per CU, two waves per SIMD: causal T = 8192 and 16384 8% faster than 4 waves
+  // with K^T in registers; the same layout at 2 waves per workgroup, below 2048, was 4-7% slower
+  // than the register one), 4-wave ones at d <= 64 (which already run two waves per SIMD).
   long long seen = p.causal ? p.Tk / 2 : p.Tk;
   if (p.window > 0 && p.window < seen) seen = p.window;
   if (seen <= 2048) return launch_grads<D, 4, 2>(p, pk, ws, c, stream);
-  return launch_grads<D, 8, 4>(p, pk, ws, c, stream);
+  if constexpr (D >= 128) {
+    return launch_grads<D, 8, 8>(p, pk, ws, c, stream);
+  } else {
+    return launch_grads<D, 8, 4>(p, pk, ws, c, stream);
+  }
 }
 
 hipError_t launch_any(const BwdProblem& p, const Packed* pk, float* ws, hipStream_t stream) {
