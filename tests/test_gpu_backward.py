@@ -132,6 +132,32 @@ def test_scales(fa, scale):
     bwd_case(fa, cfg, scale=scale)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("shape", ["noncausal_T2100", "causal_T4400_W2100", "gqa4_Tq300_Tk2300"])
+def test_long_row_workgroups(fa, shape, d):
+    # Rows that see over 2048 keys on average select the 8-wave workgroups (at d = 128 the dK/dV
+    # kernel then keeps its K block in LDS): a ragged last key block, a window, GQA and Tk > Tq
+    # at sizes the oracle runs in full.
+    Tq, Tk, Hq, causal, W = {"noncausal_T2100": (2100, 2100, 2, False, None),
+                             "causal_T4400_W2100": (4400, 4400, 2, True, 2100),
+                             "gqa4_Tq300_Tk2300": (300, 2300, 4, False, None)}[shape]
+    # GPU forward then GPU backward, against the oracle's dense backward from Q, K, V and dO (the
+    # pages' tiled backward is too slow in fp64 at these lengths; the two are pinned equal).
+    import torch
+
+    cfg = _cfg(f"bwd long rows {shape} d{d}", 1, Hq, 1, Tq, Tk, d, causal, seed=Tk + d)
+    _say(cfg.name)
+    Q, K, V = inputs.make_inputs(cfg)
+    dO = inputs.make_grad(cfg)
+    q, k, v, do = _dev(Q), _dev(K), _dev(V), _dev(dO)
+    o, lse = fa.attn_fwd(q, k, v, causal=causal, window=W)
+    dq, dk, dv = fa.attn_bwd(q, k, v, o, lse, do, causal=causal, window=W)
+    torch.cuda.synchronize()
+    ref = oracle.dense_backward(Q, K, V, dO, causal, cfg.scale, window=W)
+    for n, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        check_grad(_np(g), r, f"{cfg.name} {n}")
+
+
 def test_keys_no_row_sees_have_zero_gradients(fa):
     # Tk > Tq with a narrow window: keys before position Tk - Tq - W + 1 are seen by no row.
     cfg = _cfg("bwd unseen keys", 1, 2, 1, 40, 300, 64, seed=8)
