@@ -698,9 +698,9 @@ hipError_t launch_grads(const BwdProblem& p, const Packed* pk, float* ws, float 
         Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
         p.window, p.scale, c, nullptr, nullptr, 0, 0);
 
-  // K in LDS for the 8-wave dK/dV workgroups at d = 128 (two waves per SIMD); elsewhere K^T in
-  // registers (one wave per SIMD at d = 128, two below)
-  constexpr bool KLDS = D >= 128 && KV_NW == 8;
+  // K in LDS for the dK/dV workgroups of 4 and 8 waves at d = 128 (two waves per SIMD); K^T in
+  // registers below (two waves per SIMD already at d <= 64)
+  constexpr bool KLDS = D >= 128 && KV_NW >= 4;
   constexpr int KV_BC = 32, KV_MINW = (KLDS || D < 128) ? 2 : 1;
   const int nkb = (p.Tk + 32 * KV_NW - 1) / (32 * KV_NW);
   const dim3 kv_grid((unsigned)(p.B * p.Hkv * nkb)), kv_block(64 * KV_NW);
@@ -736,20 +736,21 @@ hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Workgroup size by the keys an average row sees (half the longest sequence when causal, at
-  // most the window). Up to 2048: 4-wave dQ workgroups (128 query rows) and 2-wave dK/dV
-  // workgroups (64 keys), whose doubled workgroup count balances the CUs better, against 8 and
-  // 4 waves 16-21% faster on causal d = 64 and 128 at T = 1024 and 2048 and 5% on a packed
-  // batch of 35 documents up to 4096 tokens. Beyond, 8-wave dQ workgroups, which read K and V
-  // half as often per query row, and 8-wave dK/dV workgroups with the K block in LDS at d = 128
-  // (one workgroup per CU, two waves per SIMD: causal T = 8192 and 16384 8% faster than 4 waves
-  // with K^T in registers; the same layout at 2 waves per workgroup, below 2048, was 4-7% slower
-  // than the register one), 4-wave ones at d <= 64 (which already run two waves per SIMD).
+  // most the window). Up to 2048: 4-wave dQ workgroups (128 query rows), whose doubled workgroup
+  // count balances the CUs better (against 8 waves 16-21% faster on causal d = 64 and 128 at
+  // T = 1024 and 2048 and 5% on a packed batch of 35 documents up to 4096 tokens). Beyond,
+  // 8-wave dQ workgroups, which read K and V half as often per query row. dK/dV workgroups at
+  // d = 128 keep their K block in LDS and run two waves per SIMD: 4 waves up to 2048 (3-9%
+  // faster than 2 waves with K^T in registers at T = 1024 to 4096), 8 beyond (one workgroup per
+  // CU: causal T = 8192 and 16384 8% faster than 4 waves with K^T in registers). At d <= 64, 2
+  // and 4 waves with K^T in registers.
   long long seen = p.causal ? p.Tk / 2 : p.Tk;
   if (p.window > 0 && p.window < seen) seen = p.window;
-  if (seen <= 2048) return launch_grads<D, 4, 2>(p, pk, ws, c, stream);
   if constexpr (D >= 128) {
+    if (seen <= 2048) return launch_grads<D, 4, 4>(p, pk, ws, c, stream);
     return launch_grads<D, 8, 8>(p, pk, ws, c, stream);
   } else {
+    if (seen <= 2048) return launch_grads<D, 4, 2>(p, pk, ws, c, stream);
     return launch_grads<D, 8, 4>(p, pk, ws, c, stream);
   }
 }
