@@ -15,9 +15,10 @@
 //    streams the K and V tiles of its head; per tile S^T and dP^T come from two MFMA products
 //    against Q^T and dO^T held in registers, dS is formed on the VALU, and dQ^T += K^T dS^T
 //    reads the same K tile transposed.
-//  * bwd_dkdv_kernel (key-block outer loop): a lane owns a key and holds V^T in registers; the
-//    workgroup's K rows sit in LDS for its whole life (read as the K^T operand), which keeps the
-//    kernel within 256 registers and so at two waves per SIMD. It streams the Q, dO and (L, D)
+//  * bwd_dkdv_kernel (key-block outer loop): a lane owns a key and holds V^T in registers; at
+//    d = 128 the workgroup's K rows sit in LDS for its whole life (read as the K^T operand), which
+//    keeps the kernel within 256 registers and so at two waves per SIMD (K^T stays in registers
+//    at d <= 64, which fits two waves per SIMD anyway). It streams the Q, dO and (L, D)
 //    tiles of every query head of its group, forms S and dP, then dV^T += dO^T P and
 //    dK^T += Q^T dS. dK and dV of a key are accumulated in registers over all the query heads
 //    that share it, so GQA needs no reduction pass.
