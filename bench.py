@@ -9,17 +9,28 @@ One step is one pass of the whole hot path on synthetic, seeded inputs already r
 Each call is bracketed by HIP events recorded on the stream the kernels are launched on. The
 headline value is the prefill rate in TFLOP/s from the median call time, counting 4*B*H*T^2*d
 halved for the causal mask; the decode rate is reported as algorithmic HBM bytes per second
-(K and V read once, Q read, O and LSE written). Mean, p10 and p90 call times are reported too.
+(K and V read once, Q read, O and LSE written). Every step's call times are in the line
+(`ms_steps`), with their median, mean, p10 and p90.
 
-After the timed steps, and outside them: the library's two probes (matrix-core rate on
-register operands, nontemporal HBM read rate) give the achievable rates the two kernels are also
-quoted against; then the sliding-window variants of both calls (window 4096, work of the visible
-(query, key) pairs only), a packed batch of variable-length documents (attn_fwd_varlen and
-attn_bwd_varlen, 32768 tokens), the decode call over a paged copy of its cache (attn_fwd_paged,
-16-position pages in a random order, checked bitwise equal to the contiguous result) and the
-backward of the prefill call (attn_bwd, seeded upstream gradient, 10*B*H*T^2*d/2 FLOPs) are timed.
-With the CPU baseline on, the fp64 oracle is also timed on bounded samples of those calls
-(`cpu_oracle_beside`). One JSON line is printed.
+Warm-up: the W steps asked for, then, if those took less than CLOCK_WARMUP_MS of GPU time, more
+of the same steps until that much has run (the clock climbs from its idle state over the first
+tens of milliseconds of back-to-back work). The extra steps are untimed and reported in the line
+(`warmup_extra`).
+
+After the timed steps, and outside them: the probes (matrix-core rate on register operands,
+nontemporal HBM read rate; a separate library, libfattn_probe.so) give the achievable rates the
+two kernels are also quoted against; then the sliding-window variants of both calls (window
+4096, work of the visible (query, key) pairs only), a packed batch of variable-length documents
+(attn_fwd_varlen and attn_bwd_varlen, 32768 tokens), the decode call over a paged copy of its
+cache (attn_fwd_paged, 16-position pages in a random order, checked bitwise equal to the
+contiguous result) and the backward of the prefill call (attn_bwd, seeded upstream gradient,
+10*B*H*T^2*d/2 FLOPs) are timed.
+
+With the CPU baseline on (the default), the fp64 oracle is timed first, before this process
+touches the GPU, one child process per measurement: each of the five workloads on all host cores
+(the large ones on a stated subset of heads or sequences, scaled by their count, which is exact
+because they cost the same), and the small ones and the decode on one core too. One JSON line is
+printed.
 
     python bench.py --calibrate-copy BYTES
 
@@ -47,6 +58,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
 PREFILL = "bf16_causal_b1_h32_t8192_d128"
 DECODE = "bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128"
 PROFILES = os.path.join(ROOT, "profiles")
+PROBE_LIB = os.path.join(ROOT, "io_aware_tiled_amd", "libfattn_probe.so")
+CLOCK_WARMUP_MS = 300.0
 
 
 def prefill_flops(B, H, Tq, Tk, d, causal):
@@ -118,15 +131,23 @@ def time_calls(torch, fn, warmup, reps):
     return [e[0].elapsed_time(e[1]) for e in ev]
 
 
-def probes(fa, torch):
-    """Matrix-core TFLOP/s and HBM read GB/s of the library's probes (best of a few launches)."""
+def probes(torch):
+    """Matrix-core TFLOP/s and HBM read GB/s of the probes (best of a few launches)."""
+    import ctypes
+
+    plib = ctypes.CDLL(PROBE_LIB)
+    plib.probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    plib.probe_mfma_bf16.restype = ctypes.c_int
+    plib.probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_void_p]
+    plib.probe_hbm_read.restype = ctypes.c_int
     wgs, iters = 2048, 100
     out = torch.empty(wgs * 512, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
 
     def mfma():
-        rc = fa.lib.fattn_probe_mfma(out.data_ptr(), wgs, iters, stream)
-        assert rc == fa.FATTN_OK, rc
+        rc = plib.probe_mfma_bf16(out.data_ptr(), wgs, iters, stream)
+        assert rc == 0, rc
 
     t = time_calls(torch, mfma, 3, 5)
     mfma_tflops = wgs * 8 * 32 * iters * 32768.0 / (min(t) * 1e-3) / 1e12
@@ -136,8 +157,8 @@ def probes(fa, torch):
     words = torch.empty(rwgs * 4, dtype=torch.int32, device="cuda")
 
     def read():
-        rc = fa.lib.fattn_probe_hbm_read(buf.data_ptr(), nbytes, words.data_ptr(), rwgs, stream)
-        assert rc == fa.FATTN_OK, rc
+        rc = plib.probe_hbm_read(buf.data_ptr(), nbytes, words.data_ptr(), rwgs, stream)
+        assert rc == 0, rc
 
     t = time_calls(torch, read, 20, 10)
     read_gbs = nbytes / (min(t) * 1e-3) / 1e9
@@ -201,102 +222,192 @@ def traffic_for(kernel_source, key):
     return None
 
 
-def cpu_baseline(budget_s=12.0, max_heads=32):
-    """The fp64 oracle timed on the host cores on a bounded sample of the prefill workload."""
-    import numpy as np  # noqa: F401
-    from threadpoolctl import threadpool_info
+def counters_for(kernel_source, key):
+    """Utilisation counters of the dominant kernel of a call (matrix-core busy share, LDS bank
+    conflict cycles per LDS-active cycle, HBM bytes per launch), read from the `counter-record:`
+    line of the committed profile summaries; None when no summary has it or the kernel source
+    changed since the counters were taken."""
+    import glob
 
-    import oracle
-    from tests import inputs
-
-    cfg = inputs.CONFIGS[PREFILL]
-    heads, elapsed = 0, 0.0
-    while heads < max_heads and (heads == 0 or elapsed < budget_s):
-        q = inputs.head_slice(cfg, inputs.Q_ID, 0, heads)
-        k = inputs.head_slice(cfg, inputs.K_ID, 0, heads)
-        v = inputs.head_slice(cfg, inputs.V_ID, 0, heads)
-        t0 = time.perf_counter()
-        oracle.dense_head(q, k, v, cfg.causal, cfg.scale)
-        elapsed += time.perf_counter() - t0
-        heads += 1
-    flops = prefill_flops(1, heads, cfg.Tq, cfg.Tk, cfg.d, cfg.causal)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{heads} of 32 heads of the causal T=8192 d=128 prefill, all 8192 rows "
-                      f"each, fp64 dense (S and P materialised), {elapsed:.2f} s; TFLOP/s with "
-                      f"the same causal-halved FLOP count as the GPU figure",
-            "seconds": elapsed, "host_cpus": len(os.sched_getaffinity(0))}
+    want = source_hash(kernel_source)
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if line.startswith("counter-record:"):
+                    try:
+                        rec = json.loads(line.split(":", 1)[1])
+                    except ValueError:
+                        continue
+                    if (rec.get("key") == key and rec.get("source") == kernel_source
+                            and rec.get("source_sha256_16") == want):
+                        return {k: v for k, v in rec.items() if k not in ("key", "source")}
+    return None
 
 
-def oracle_beside(budget_s=3.0):
-    """The fp64 oracle timed on bounded samples of the other measured calls (sliding window,
-    packed prefill, paged decode, backward), each in the unit of its GPU figure: heads (or
-    sequences) are added until `budget_s` seconds of oracle time have run."""
+# ---- the CPU oracle, timed in child processes (one per measurement) before the GPU is touched
+
+# name -> (config, what is timed, units timed, units in the workload, unit name)
+ORACLE_CASES = {
+    "C1": ("f32_causal_b1_h4_t128_d32", "all 4 heads", None, None, "heads"),
+    "C2": ("bf16_causal_b4_h16_t1024_d64", "all 64 heads", None, None, "heads"),
+    "C3": (PREFILL, "all 32 heads", None, None, "heads"),
+    "C4": (DECODE, "sequences 0-7 of 64 (all 64 query heads each)", 8, 64, "sequences"),
+    "C5": ("bf16_gqa_causal_b2_hq32_hkv8_t16384_d128",
+           "query heads 0 and 1 of sequence 0 (kv head 0) of 64 heads", 2, 64, "heads"),
+}
+# the calls timed after the steps, each on a bounded sample: name -> sample description
+BESIDE_CASES = {
+    "sliding_window_prefill": "heads 0-3 of 32 of the W=4096 causal T=8192 d=128 prefill, fp64 "
+                              "dense",
+    "backward": "heads 0-2 of 32 of the causal T=8192 d=128 backward, fp64 chain rule with P "
+                "materialised",
+    "varlen": "head 0 of the first two documents of the packed batch, fp64 dense per document",
+    "paged_decode": "sequences 0-1 of 64 of the paged GQA decode (16-position pages), gather then "
+                    "fp64 dense",
+}
+
+
+def _slices(cfg, which, bs, hs):
     import numpy as np
 
+    from tests import inputs
+
+    T = cfg.Tq if which == inputs.Q_ID else cfg.Tk
+    out = np.empty((len(bs), len(hs), T, cfg.d), np.float32)
+    for i, b in enumerate(bs):
+        for j, h in enumerate(hs):
+            out[i, j] = inputs.head_slice(cfg, which, b, h)
+    return out
+
+
+def oracle_case(name):
+    """In a child process: generate the inputs of one measurement (untimed), time the oracle on
+    them and return {"seconds", "threads", "timed", "total", "work", "unit"}: `work` is the
+    algorithmic FLOPs (or bytes, for a decode) of the timed part."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
     import oracle
     from tests import inputs
 
-    from threadpoolctl import threadpool_info
-
-    cfg = inputs.CONFIGS[PREFILL]
-    out = {"kind": "oracle",
-           "cores": max([i.get("num_threads", 1) for i in threadpool_info()] or [1])}
-
-    def heads_until(fn):
-        n, el = 0, 0.0
-        while n < cfg.Hq and (n == 0 or el < budget_s):
-            args = fn(n)
+    res = {}
+    if name in ORACLE_CASES:
+        key, _, timed, total, _ = ORACLE_CASES[name]
+        cfg = inputs.CONFIGS[key]
+        bs, hq, hk = range(cfg.B), range(cfg.Hq), range(cfg.Hkv)
+        if name == "C4":
+            bs = range(timed)
+        elif name == "C5":
+            bs, hq, hk = [0], [0, 1], [0]
+        Q = _slices(cfg, inputs.Q_ID, bs, hq)
+        K = _slices(cfg, inputs.K_ID, bs, hk)
+        V = _slices(cfg, inputs.V_ID, bs, hk)
+        t0 = time.perf_counter()
+        oracle.dense_attention(Q, K, V, cfg.causal, cfg.scale)
+        el = time.perf_counter() - t0
+        if name == "C4":
+            work, unit = decode_bytes(len(bs), cfg.Hq, cfg.Hkv, cfg.Tk, cfg.d), "bytes"
+        else:
+            work = prefill_flops(len(bs), len(hq), cfg.Tq, cfg.Tk, cfg.d, cfg.causal)
+            unit = "FLOPs"
+        n = len(bs) if name == "C4" else len(bs) * len(hq)
+        res = {"timed": n, "total": cfg.B if name == "C4" else cfg.B * cfg.Hq}
+    else:
+        cfg = inputs.CONFIGS[PREFILL]
+        if name == "sliding_window_prefill":
+            W, hs = 4096, range(4)
+            Q, K, V = (_slices(cfg, w, [0], hs) for w in (inputs.Q_ID, inputs.K_ID, inputs.V_ID))
             t0 = time.perf_counter()
-            args[0](*args[1:])
-            el += time.perf_counter() - t0
-            n += 1
-        return n, el
+            oracle.dense_attention(Q, K, V, True, cfg.scale, window=W)
+            el = time.perf_counter() - t0
+            work, unit = 4.0 * cfg.d * len(hs) * window_pairs(cfg.Tq, W), "FLOPs"
+        elif name == "backward":
+            hs = range(3)
+            Q, K, V = (_slices(cfg, w, [0], hs) for w in (inputs.Q_ID, inputs.K_ID, inputs.V_ID))
+            dO = np.stack([inputs.grad_slice(cfg, 0, h) for h in hs])[None]
+            t0 = time.perf_counter()
+            oracle.dense_backward(Q, K, V, dO, True, cfg.scale)
+            el = time.perf_counter() - t0
+            work, unit = backward_flops(1, len(hs), cfg.Tq, cfg.Tk, cfg.d, True), "FLOPs"
+        elif name == "varlen":
+            lens = varlen_doc_lengths(VARLEN_TOKENS, 128, 8192, VARLEN_SEED)[:2]
+            vc = inputs.AttnConfig("varlen oracle sample", B=1, Hq=1, Hkv=1, Tq=1, Tk=1, d=cfg.d,
+                                   dtype="bf16", causal=True, dist="normal", seed=VARLEN_SEED)
+            Q, K, V, cq, ck = inputs.make_packed(vc, lens)
+            t0 = time.perf_counter()
+            oracle.varlen_attention(Q, K, V, cq, ck, True, cfg.scale)
+            el = time.perf_counter() - t0
+            work, unit = sum(prefill_flops(1, 1, m, m, cfg.d, True) for m in lens), "FLOPs"
+        elif name == "paged_decode":
+            dc = inputs.CONFIGS[DECODE].replace(B=2, name="paged oracle sample")
+            Qd, _, _ = inputs.make_inputs(dc)
+            Kc, Vc, table, sl = inputs.make_paged(dc, 16, [dc.Tk] * dc.B)
+            t0 = time.perf_counter()
+            oracle.paged_decode(Qd[:, :, 0], Kc, Vc, table, sl, dc.scale)
+            el = time.perf_counter() - t0
+            work, unit = decode_bytes(dc.B, dc.Hq, dc.Hkv, dc.Tk, dc.d), "bytes"
+        else:
+            raise ValueError(name)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    res.update({"seconds": el, "threads": threads, "work": work, "unit": unit,
+                "cpus": len(os.sched_getaffinity(0))})
+    return res
 
-    def head(h):
-        return (inputs.head_slice(cfg, inputs.Q_ID, 0, h), inputs.head_slice(cfg, inputs.K_ID, 0, h),
-                inputs.head_slice(cfg, inputs.V_ID, 0, h))
 
-    W = 4096
-    n, el = heads_until(lambda h: (lambda q, k, v: oracle.dense_head(q, k, v, True, cfg.scale,
-                                                                      window=W), *head(h)))
-    out["sliding_window_prefill"] = {
-        "value": 4.0 * cfg.d * n * window_pairs(cfg.Tq, W) / el / 1e12, "unit": "TFLOP/s",
-        "sample": f"{n} heads of the W=4096 T=8192 d=128 prefill, fp64 dense, {el:.2f} s"}
+def _oracle_child(name, one_core):
+    """Runs `bench.py --oracle-case name` as a child process (all host cores, or one)."""
+    import subprocess
 
-    n, el = heads_until(lambda h: (lambda q, k, v, do: oracle.dense_backward_head(
-        q, k, v, do, True, cfg.scale), *head(h), inputs.grad_slice(cfg, 0, h)))
-    out["backward"] = {
-        "value": backward_flops(1, n, cfg.Tq, cfg.Tk, cfg.d, True) / el / 1e12, "unit": "TFLOP/s",
-        "sample": f"{n} heads of the causal T=8192 d=128 backward, fp64 chain rule with P "
-                  f"materialised, {el:.2f} s"}
+    env = dict(os.environ)
+    cmd = [sys.executable, os.path.abspath(__file__), "--oracle-case", name]
+    if one_core:
+        for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+            env[v] = "1"
+        cmd.append("--one-core")
+    r = subprocess.run(cmd, capture_output=True, text=True, env=env, timeout=300)
+    if r.returncode != 0:
+        raise RuntimeError(f"oracle child {name} failed ({r.returncode}): {r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
-    lens = varlen_doc_lengths(VARLEN_TOKENS, 128, 8192, VARLEN_SEED)
-    vc = inputs.AttnConfig("varlen oracle sample", B=1, Hq=1, Hkv=1, Tq=1, Tk=1, d=cfg.d,
-                           dtype="bf16", causal=True, dist="normal", seed=VARLEN_SEED)
-    Q, K, V, cq, ck = inputs.make_packed(vc, lens[:2])
-    t0 = time.perf_counter()
-    oracle.varlen_attention(Q, K, V, cq, ck, True, cfg.scale)
-    el = time.perf_counter() - t0
-    out["varlen"] = {
-        "value": sum(prefill_flops(1, 1, m, m, cfg.d, True) for m in lens[:2]) / el / 1e12,
-        "unit": "TFLOP/s",
-        "sample": f"one head of the first two documents ({lens[0]} and {lens[1]} tokens) of the "
-                  f"packed batch, fp64 dense per document, {el:.2f} s"}
 
-    dc = inputs.CONFIGS[DECODE].replace(B=2, name="paged oracle sample")
-    Qd, _, _ = inputs.make_inputs(dc)
-    Kc, Vc, table, sl = inputs.make_paged(dc, 16, [dc.Tk] * dc.B)
-    t0 = time.perf_counter()
-    oracle.paged_decode(Qd[:, :, 0], Kc, Vc, table, sl, dc.scale)
-    el = time.perf_counter() - t0
-    out["paged_decode"] = {
-        "value": decode_bytes(dc.B, dc.Hq, dc.Hkv, dc.Tk, dc.d) / el / 1e9, "unit": "GB/s",
-        "sample": f"2 of the 64 sequences of the paged GQA decode (16-position pages), gather then "
-                  f"fp64 dense, {el:.2f} s"}
-    del np
-    return out
+def cpu_oracle_leg():
+    """The oracle timed per workload (all cores; one core for the three small ones), then on
+    samples of the calls timed after the steps. Returns (cpu_baseline, per_config, beside)."""
+    per = {}
+    for name, (key, what, timed, total, unit) in ORACLE_CASES.items():
+        print(f"[bench] CPU oracle {name} ({key})", file=sys.stderr, flush=True)
+        r = _oracle_child(name, False)
+        scale = r["total"] / r["timed"]
+        rate = r["work"] / r["seconds"]
+        e = {"config": key, "timed": what, "threads": r["threads"], "host_cpus": r["cpus"],
+             "seconds": round(r["seconds"], 4),
+             "seconds_whole_workload": round(r["seconds"] * scale, 4),
+             "extrapolated": scale != 1,
+             ("gbs" if r["unit"] == "bytes" else "tflops"):
+                 rate / 1e9 if r["unit"] == "bytes" else rate / 1e12}
+        if name in ("C1", "C2", "C4"):
+            r1 = _oracle_child(name, True)
+            e["seconds_one_core"] = round(r1["seconds"], 4)
+            e["seconds_one_core_whole_workload"] = round(r1["seconds"] * scale, 4)
+        per[name] = e
+    beside = {}
+    for name, what in BESIDE_CASES.items():
+        print(f"[bench] CPU oracle beside: {name}", file=sys.stderr, flush=True)
+        r = _oracle_child(name, False)
+        rate = r["work"] / r["seconds"]
+        beside[name] = {"value": rate / 1e9 if r["unit"] == "bytes" else rate / 1e12,
+                        "unit": "GB/s" if r["unit"] == "bytes" else "TFLOP/s",
+                        "cores": r["threads"], "kind": "oracle",
+                        "sample": f"{what}, {r['seconds']:.2f} s"}
+    c3 = per["C3"]
+    head = {"value": c3["tflops"], "unit": "TFLOP/s", "cores": c3["threads"], "kind": "oracle",
+            "sample": f"the whole causal T=8192 d=128 prefill (32 heads, all 8192 rows each), fp64 "
+                      f"dense with S and P materialised, {c3['seconds']:.2f} s in its own process; "
+                      f"the matrix products use {c3['threads']} BLAS threads, the exponentials and "
+                      f"other elementwise steps one; TFLOP/s with the causal-halved FLOP count of "
+                      f"the GPU figure",
+            "seconds": c3["seconds"], "host_cpus": c3["host_cpus"]}
+    return head, per, beside
 
 
 def _r(d):
@@ -323,7 +434,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-baseline", choices=["auto", "off"], default="auto")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    # internal: one oracle measurement in a child process (see cpu_oracle_leg)
+    ap.add_argument("--oracle-case", default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--one-core", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.oracle_case:
+        if args.one_core:
+            os.sched_setaffinity(0, {min(os.sched_getaffinity(0))})
+        print(json.dumps(oracle_case(args.oracle_case)), flush=True)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -331,6 +451,11 @@ def main():
               "libfattn has no multi-GPU path; shard (batch, kv-head) groups across GPUs "
               "with one process each instead.", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU oracle first: its child processes start before this process touches the GPU
+    cpu = per_config = beside = None
+    if args.cpu_baseline == "auto" and not args.calibrate_copy:
+        cpu, per_config, beside = cpu_oracle_leg()
 
     import torch
 
@@ -361,9 +486,27 @@ def main():
         fa.attn_fwd(q4, k4, v4, causal=dc.causal, scale=dc.scale, out=o4, lse=l4)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record()
     for _ in range(args.warmup):
         step()
+    w1.record()
     torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) if args.warmup else 0.0
+    # more untimed steps until CLOCK_WARMUP_MS of back-to-back work has run (reported)
+    extra, extra_ms = 0, 0.0
+    while warm_ms + extra_ms < CLOCK_WARMUP_MS:
+        w0.record()
+        for _ in range(10):
+            step()
+        w1.record()
+        torch.cuda.synchronize()
+        extra += 10
+        extra_ms += w0.elapsed_time(w1)
+    if extra:
+        print(f"[bench] {extra} more warm-up steps ({extra_ms:.0f} ms)", file=sys.stderr,
+              flush=True)
 
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -378,8 +521,9 @@ def main():
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pst = stats_ms([e[0].elapsed_time(e[1]) for e in ev])
-    dst = stats_ms([e[1].elapsed_time(e[2]) for e in ev])
+    p_steps = [e[0].elapsed_time(e[1]) for e in ev]
+    d_steps = [e[1].elapsed_time(e[2]) for e in ev]
+    pst, dst = stats_ms(p_steps), stats_ms(d_steps)
     prefill_ms, decode_ms = pst["median"], dst["median"]
     if not (bool(torch.isfinite(o3).all()) and bool(torch.isfinite(o4).all())):
         print("non-finite output", file=sys.stderr)
@@ -392,7 +536,7 @@ def main():
 
     # ---- outside the timed steps: achievable rates, then the sliding-window variants
     print("[bench] probes and sliding-window calls", file=sys.stderr, flush=True)
-    pr = probes(fa, torch)
+    pr = probes(torch)
     W = 4096
     sw_p = stats_ms(time_calls(torch, lambda: fa.attn_fwd(q3, k3, v3, causal=True, scale=pc.scale,
                                                          out=o3, lse=l3, window=W), 10, 20))
@@ -482,14 +626,6 @@ def main():
     bw_tflops = bw_flops / (bw["median"] * 1e-3) / 1e12
     del do3, dq3, dk3, dv3
 
-    cpu = None
-    beside = None
-    if args.cpu_baseline == "auto":
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline()
-        print("[bench] timing the CPU oracle beside the other calls", file=sys.stderr, flush=True)
-        beside = oracle_beside()
-
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -497,6 +633,11 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_extra": {"steps": extra, "ms": round(extra_ms, 1),
+                         "why": f"untimed steps after the {args.warmup} asked for, until "
+                                f"{CLOCK_WARMUP_MS:.0f} ms of back-to-back work had run (the "
+                                f"{args.warmup} took {warm_ms:.1f} ms): the clock climbs "
+                                f"from its idle state over the first tens of ms"},
         "ms_per_step": round(wall * 1e3 / K, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -513,18 +654,22 @@ def main():
         "prefill": {"ms": round(prefill_ms, 4), "tflops": round(tflops, 2),
                     "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
                     "pct_of_probe": round(100 * tflops / pr["mfma_bf16_tflops"], 2),
-                    "flops_per_call": flops, "ms_stats": _r(pst)},
+                    "flops_per_call": flops, "ms_stats": _r(pst),
+                    "ms_steps": [round(x, 4) for x in p_steps]},
         "decode": {"ms": round(decode_ms, 4), "gbs": round(gbs, 1),
                    "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
                    "pct_of_probe": round(100 * gbs / pr["hbm_read_gbs"], 2),
                    "bytes_per_call": dbytes, "ms_stats": _r(dst),
+                   "ms_steps": [round(x, 4) for x in d_steps],
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                "traffic": traffic_for("decode_bf16.hip", "decode")}},
+                                "traffic": traffic_for("decode_bf16.hip", "decode"),
+                                "counters": counters_for("decode_bf16.hip", "decode")}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for("prefill_bf16.hip", "prefill")},
+                     "traffic": traffic_for("prefill_bf16.hip", "prefill"),
+                     "counters": counters_for("prefill_bf16.hip", "prefill")},
         "probes": pr,
         "sliding_window": {
             "window": W,
@@ -572,8 +717,10 @@ def main():
             "work": "10*B*H*T^2*d/2: the five products S, dP, dV, dK, dQ; the kernels run seven "
                     "(S and dP once in the dQ kernel and once in the dK/dV kernel)",
             "traffic": traffic_for("backward_bf16.hip", "backward"),
+            "counters": counters_for("backward_bf16.hip", "backward"),
         },
         "cpu_baseline": cpu,
+        "cpu_oracle_per_config": per_config,
         "cpu_oracle_beside": beside,
     }
     print(json.dumps(line), flush=True)

@@ -27,6 +27,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility; exactly the calls declared here are
+   exported. */
+#pragma GCC visibility push(default)
+
 /* Return codes. */
 #define FATTN_OK 0
 #define FATTN_ERR_INVALID (-1)     /* an argument is out of its documented range */
@@ -264,28 +268,7 @@ int fattn_version(void);
  */
 int fattn_release(void);
 
-/*
- * Measurement probes, not part of the attention path; bench.py uses them to quote the kernels'
- * rates against what this chip reaches on trivial work as well as against the published peaks.
- *
- * fattn_probe_mfma: enqueues `workgroups` workgroups of 8 wavefronts on `stream`; each
- * wavefront issues 32 * iters v_mfma_f32_32x32x16_bf16 (32768 FLOPs each) in four independent
- * chains on register operands, then writes one float per thread to `out` (device memory of at
- * least workgroups * 512 floats, owned by the caller). FLOPs per launch:
- * workgroups * 8 * 32 * iters * 32768.
- *
- * fattn_probe_hbm_read: enqueues `workgroups` workgroups of 256 threads that read the `bytes`
- * bytes at device pointer `buf` once with 16-byte nontemporal loads, workgroup w the w-th of
- * `workgroups` equal contiguous chunks, and write one word per wavefront to `out` (at least
- * workgroups * 4 words). `buf` must be 16-byte aligned and `bytes` a
- * positive multiple of 16.
- *
- * Both return FATTN_ERR_INVALID for a NULL pointer or a non-positive count (and, for the read
- * probe, a misaligned buffer or size), FATTN_ERR_HIP for a launch failure, else FATTN_OK.
- */
-int fattn_probe_mfma(float* out, int workgroups, int iters, void* stream);
-int fattn_probe_hbm_read(const void* buf, size_t bytes, unsigned* out, int workgroups,
-                         void* stream);
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

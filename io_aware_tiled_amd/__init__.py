@@ -83,10 +83,6 @@ lib.attn_fwd_paged.restype = _i
 lib.attn_bwd.argtypes = [_vp] * 9 + [_i] * 8 + [_f, _i, _vp]
 lib.attn_bwd.restype = _i
 lib.attn_fwd_plan.argtypes = [_i] * 8 + [ctypes.POINTER(FattnCfg), ctypes.POINTER(FattnCfg)]
-lib.fattn_probe_mfma.argtypes = [_vp, _i, _i, _vp]
-lib.fattn_probe_mfma.restype = _i
-lib.fattn_probe_hbm_read.argtypes = [_vp, ctypes.c_size_t, _vp, _i, _vp]
-lib.fattn_probe_hbm_read.restype = _i
 lib.attn_fwd_plan.restype = _i
 lib.fattn_strerror.argtypes = [_i]
 lib.fattn_strerror.restype = ctypes.c_char_p
@@ -123,6 +119,21 @@ def fattn_release() -> None:
     rc = lib.fattn_release()
     if rc != FATTN_OK:
         raise FattnError(rc)
+
+
+def check_out(name: str, t, shape, dtype, device) -> None:
+    """A caller-supplied output buffer must be exactly what the kernels write into: the expected
+    shape and dtype, contiguous, on the inputs' device. Raises ValueError (TypeError for the
+    dtype) before anything is launched; the kernels would otherwise write past a short buffer
+    or through a strided view."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
 
 
 def _make_cfg(cfg) -> Optional[FattnCfg]:
@@ -205,8 +216,10 @@ def attn_fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, out=N
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    check_out("out", out, q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    check_out("lse", lse, (B, Hq, Tq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -261,6 +274,8 @@ def attn_bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] =
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        check_out(name, t, ref.shape, torch.bfloat16, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -313,8 +328,10 @@ def attn_fwd_paged(q, k_cache, v_cache, block_table, seq_lens, scale: Optional[f
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    check_out("out", out, q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    check_out("lse", lse, (B, Hq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -372,8 +389,10 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    check_out("out", out, q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    check_out("lse", lse, (Hq, total_q), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -440,6 +459,8 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        check_out(name, t, ref.shape, torch.bfloat16, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):

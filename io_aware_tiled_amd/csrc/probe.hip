@@ -1,20 +1,28 @@
-// Measurement probes (not part of the attention path): the matrix-core and HBM-read rates this
-// chip reaches on trivial work, so that the attention kernels' rates can be quoted against what
-// is achievable as well as against the published peaks.
+// Measurement probes, built into their own library (libfattn_probe.so) that only the benchmark
+// loads: the matrix-core and HBM-read rates this chip reaches on trivial work, so that the
+// attention kernels' rates can be quoted against what is achievable as well as against the
+// published peaks. Not part of libfattn or of its C ABI.
 //
-//  * fattn_probe_mfma: every wavefront runs four independent chains of
-//    v_mfma_f32_32x32x16_bf16 (the prefill kernel's instruction) on register operands, eight
-//    wavefronts per workgroup; 32768 FLOPs per instruction.
-//  * fattn_probe_hbm_read: 16-byte nontemporal loads over a buffer (the decode kernel's load
-//    form), one contiguous chunk per workgroup, one XOR-reduced word stored per wavefront.
+//  int probe_mfma_bf16(float* out, int workgroups, int iters, void* stream);
+//    Enqueues `workgroups` workgroups of 8 wavefronts on `stream`; every wavefront runs four
+//    independent chains of v_mfma_f32_32x32x16_bf16 (the prefill kernel's instruction, 32768
+//    FLOPs each), 32 * iters of them, on register operands, then writes one float per thread to
+//    `out` (device memory of at least workgroups * 512 floats, owned by the caller).
+//    FLOPs per launch: workgroups * 8 * 32 * iters * 32768.
+//  int probe_hbm_read(const void* buf, size_t bytes, unsigned* out, int workgroups, void* stream);
+//    Enqueues `workgroups` workgroups of 256 threads that read the `bytes` bytes at device
+//    pointer `buf` once with 16-byte nontemporal loads (the decode kernel's load form),
+//    workgroup w the w-th of `workgroups` equal contiguous chunks, and write one XOR-reduced word
+//    per wavefront to `out` (at least workgroups * 4 words). `buf` must be 16-byte aligned and
+//    `bytes` a positive multiple of 16.
+//  Both return -1 for a NULL pointer or a non-positive count (and, for the read probe, a
+//  misaligned buffer or size), -3 for a launch failure, else 0.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
 
-#include "fattn.h"
 
-namespace fattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -69,24 +77,25 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
 }
 
 }  // namespace
-}  // namespace fattn
 
-using namespace fattn;
+constexpr int kOk = 0, kInvalid = -1, kLaunch = -3;
 
-extern "C" int fattn_probe_mfma(float* out, int workgroups, int iters, void* stream) {
-  if (!out || workgroups <= 0 || iters <= 0) return FATTN_ERR_INVALID;
+#define PROBE_API extern "C" __attribute__((visibility("default")))
+
+PROBE_API int probe_mfma_bf16(float* out, int workgroups, int iters, void* stream) {
+  if (!out || workgroups <= 0 || iters <= 0) return kInvalid;
   hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)workgroups), dim3(512), 0,
                      reinterpret_cast<hipStream_t>(stream), out, iters);
-  return hipGetLastError() == hipSuccess ? FATTN_OK : FATTN_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? kOk : kLaunch;
 }
 
-extern "C" int fattn_probe_hbm_read(const void* buf, size_t bytes, unsigned* out,
-                                    int workgroups, void* stream) {
+PROBE_API int probe_hbm_read(const void* buf, size_t bytes, unsigned* out, int workgroups,
+                             void* stream) {
   if (!buf || !out || workgroups <= 0 || bytes < 16 || (bytes & 15) != 0 ||
       (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
-    return FATTN_ERR_INVALID;
+    return kInvalid;
   hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)workgroups), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf),
                      bytes / 16, out);
-  return hipGetLastError() == hipSuccess ? FATTN_OK : FATTN_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? kOk : kLaunch;
 }

@@ -25,8 +25,8 @@ from .attention import (  # noqa: F401
     dense_head,
     merge_partials,
     online_logsumexp_trace,
-    online_softmax,
-    online_softmax_weighted_sum,
+    stream_softmax,
+    stream_weighted_sum,
     tiled_attention,
     tiled_head,
 )

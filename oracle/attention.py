@@ -273,57 +273,55 @@ def merge_partials(o_parts, lse_parts):
 # One-dimensional units of the recurrence.
 # --------------------------------------------------------------------------------------------
 
-def online_softmax_weighted_sum(x, V, block_size: int = 4):
-    """sum_i softmax(x)_i V[i] in one streaming pass over blocks of logits.
+def _block_rebases(z: np.ndarray, width: int):
+    """Walk the 1-D logits z in blocks of ``width``: for each block [lo, hi) yield (lo, hi, top,
+    rescale), where top is the running maximum once the block is included and rescale =
+    exp(previous top - top) is the factor every sum gathered over earlier blocks is multiplied
+    by (0 before any block, when nothing has been gathered). This is the correction factor of
+    "4.2 FlashAttention I" (section "The key idea: a running max and a correction factor")."""
+    top = -math.inf
+    for lo in range(0, z.shape[0], width):
+        hi = min(lo + width, z.shape[0])
+        new_top = max(top, float(z[lo:hi].max()))
+        yield lo, hi, new_top, (math.exp(top - new_top) if top > -math.inf else 0.0)
+        top = new_top
+
+
+def stream_weighted_sum(logits, values, width: int = 4):
+    """sum_i softmax(logits)_i values[i], gathered in one pass over blocks of ``width`` logits.
 
     The streaming weighted sum of "4.2 FlashAttention I" (section "A from-scratch implementation
-    and a correctness proof"): state (m, l, o); per block m' = max(m, block max),
-    alpha = exp(m - m'), p = exp(x_blk - m'), l = alpha*l + sum p, o = alpha*o + p V_blk.
+    and a correctness proof"): the normaliser and the weighted sum are both rescaled by the
+    correction factor whenever the running maximum grows, and divided once at the end.
     """
-    x, V = _f64(x), _f64(V)
-    m, l = -np.inf, 0.0
-    o = np.zeros(V.shape[1])
-    for s in range(0, x.shape[0], block_size):
-        xb, Vb = x[s:s + block_size], V[s:s + block_size]
-        m_new = max(m, xb.max())
-        alpha = math.exp(m - m_new) if m > -math.inf else 0.0
-        p = np.exp(xb - m_new)
-        l = alpha * l + p.sum()
-        o = alpha * o + p @ Vb
-        m = m_new
-    return o / l
+    z, vals = _f64(logits), _f64(values)
+    norm, acc = 0.0, np.zeros(vals.shape[1])
+    for lo, hi, top, rescale in _block_rebases(z, width):
+        w = np.exp(z[lo:hi] - top)
+        norm = rescale * norm + w.sum()
+        acc = rescale * acc + w @ vals[lo:hi]
+    return acc / norm
 
 
-def online_softmax(x, chunk: int):
-    """softmax of a 1-D vector with the max and normaliser gathered in one streaming pass.
-
-    ``online_softmax`` of "Efficient attention & KV cache" (section 3): m and l carried over
-    chunks, then exp(x - m) / l.
-    """
-    x = _f64(x)
-    m, l = -np.inf, 0.0
-    for s in range(0, x.shape[0], chunk):
-        blk = x[s:s + chunk]
-        m_new = max(m, blk.max())
-        l = l * (math.exp(m - m_new) if m > -math.inf else 0.0) + np.exp(blk - m_new).sum()
-        m = m_new
-    return np.exp(x - m) / l
+def stream_softmax(logits, width: int):
+    """softmax of a 1-D vector whose maximum and normaliser are gathered in one pass over
+    blocks of ``width`` entries ("Efficient attention & KV cache", section 3), then applied."""
+    z = _f64(logits)
+    norm, top = 0.0, -math.inf
+    for lo, hi, top, rescale in _block_rebases(z, width):
+        norm = rescale * norm + np.exp(z[lo:hi] - top).sum()
+    return np.exp(z - top) / norm
 
 
 def online_logsumexp_trace(x, block_size: int) -> List[Tuple[float, float, float]]:
-    """The (m, alpha, l) state after each block of the streaming recurrence, for hand traces.
+    """The (running max, correction factor, normaliser) after each block, for hand traces.
 
     Exercise 2 of "4.2 FlashAttention I" streams [3, 1, 6, 2] in blocks of two; the final
-    log-sum-exp is m + log(l).
+    log-sum-exp is the running max plus the log of the normaliser.
     """
-    x = _f64(x)
-    m, l = -math.inf, 0.0
-    trace = []
-    for s in range(0, x.shape[0], block_size):
-        blk = x[s:s + block_size]
-        m_new = max(m, float(blk.max()))
-        alpha = math.exp(m - m_new) if m > -math.inf else 0.0
-        l = alpha * l + float(np.exp(blk - m_new).sum())
-        m = m_new
-        trace.append((m, alpha, l))
+    z = _f64(x)
+    norm, trace = 0.0, []
+    for lo, hi, top, rescale in _block_rebases(z, block_size):
+        norm = rescale * norm + float(np.exp(z[lo:hi] - top).sum())
+        trace.append((top, rescale, norm))
     return trace

@@ -196,6 +196,10 @@ def backward_cols(q, k, v, do, keys, causal: bool, scale: Optional[float] = None
     dS_:j = P_:j * (dP_:j - D), dK_j = scale dS_:j^T Q, with D = rowsum(dO * O).
     Returns (dK [len(keys), d], dV [len(keys), d]) of this query head alone; a kv head's
     gradient is the sum over the query heads that read it.
+
+    Under a causal mask a row at position i + Tk - Tq sees key j only if j <= i + Tk - Tq, so the
+    rows before the first one that sees the smallest requested key have P = 0 in every requested
+    column and add nothing to the sums: they are left out (O and L are computed for the rest).
     """
     from .attention import dense_head
 
@@ -203,14 +207,16 @@ def backward_cols(q, k, v, do, keys, causal: bool, scale: Optional[float] = None
     Tq, d = q.shape
     Tk = k.shape[0]
     sc = _default_scale(d, scale)
-    O = np.empty((Tq, d))
-    L = np.empty(Tq)
-    for r0 in range(0, Tq, row_chunk):
+    kk = np.asarray(keys, dtype=np.int64)
+    first = max(0, int(kk.min()) - (Tk - Tq)) if (causal and kk.size) else 0
+    O = np.zeros((Tq, d))
+    L = np.zeros(Tq)
+    for r0 in range(first, Tq, row_chunk):
         rr = np.arange(r0, min(r0 + row_chunk, Tq))
         O[rr], L[rr] = dense_head(q, k, v, causal, scale, rows=rr, window=window)
     D = np.sum(do * O, axis=1)
-    kk = np.asarray(keys, dtype=np.int64)
     hide = _mask(Tq, Tk, causal, window)[:, kk]
+    hide[:first] = True
     P = np.where(hide, 0.0, np.exp(np.where(hide, 0.0, sc * (q @ k[kk].T)) - L[:, None]))
     dV = P.T @ do
     dS = P * (do @ v[kk].T - D[:, None])

@@ -35,6 +35,8 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert n in exported, n
         assert hasattr(fa.lib, n)
+    # nothing else: the internal launchers and the measurement probes stay out of the ABI
+    assert exported == set(names), sorted(exported - set(names))
 
 
 def test_version_and_strerror():

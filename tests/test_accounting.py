@@ -89,3 +89,86 @@ def test_prefill_compulsory_bytes():
         2 * (gqa - lse)
     # the attention_bytes model (Q, K, V, O of equal length, MHA) agrees without the LSE
     assert acc.attention_bytes(2, 32, 4096, 128) == full - lse
+
+
+# ---- the same figures by routes that do not restate the formulas
+
+def _bytes_of(*tensors):
+    return sum(t.numel() * t.element_size() for t in tensors)
+
+
+def _call_tensors(B, Hq, Hkv, Tq, Tk, d, device):
+    """Every tensor one forward call reads or writes, as the binding allocates them: bf16 Q, K,
+    V and O of the (B, H, T, d) layout and the fp32 LSE."""
+    import torch
+
+    bf = torch.bfloat16
+    return (torch.empty(B, Hq, Tq, d, dtype=bf, device=device),
+            torch.empty(B, Hkv, Tk, d, dtype=bf, device=device),
+            torch.empty(B, Hkv, Tk, d, dtype=bf, device=device),
+            torch.empty(B, Hq, Tq, d, dtype=bf, device=device),
+            torch.empty(B, Hq, Tq, dtype=torch.float32, device=device))
+
+
+def test_decode_bytes_are_the_bytes_of_the_generated_tensors():
+    # a small GQA decode built by the seeded generator, converted to the bf16 tensors the GPU
+    # receives, plus the O and LSE the binding allocates
+    import torch
+
+    from tests import inputs
+
+    cfg = inputs.CONFIGS["bf16_gqa_decode_b64_hq64_hkv8_tk8192_d128"].replace(B=3, Tk=257)
+    q, k, v = (inputs.to_torch(x, "bf16") for x in inputs.make_inputs(cfg))
+    o = torch.empty_like(q)
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.Tq, dtype=torch.float32)
+    assert _bytes_of(q, k, v, o, lse) == acc.decode_bytes(3, 64, 8, 257, 128)
+    # the full GQA decode, by the sizes of meta tensors of its shapes (nothing is allocated)
+    full = _call_tensors(64, 64, 8, 1, 8192, 128, "meta")
+    assert _bytes_of(*full) == acc.decode_bytes(64, 64, 8, 8192, 128) == 2149597184
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 32, 8192, 8192, 128), (2, 32, 8, 16384, 16384, 128),
+                                   (4, 16, 16, 1024, 1024, 64), (3, 8, 2, 5, 77, 32)])
+def test_prefill_compulsory_bytes_are_the_bytes_of_the_call_tensors(shape):
+    B, Hq, Hkv, Tq, Tk, d = shape
+    assert _bytes_of(*_call_tensors(B, Hq, Hkv, Tq, Tk, d, "meta")) == \
+        acc.prefill_compulsory_bytes(B, Hq, Hkv, Tq, Tk, d)
+
+
+def test_prefill_compulsory_bytes_of_generated_inputs():
+    import torch
+
+    from tests import inputs
+
+    cfg = inputs.CONFIGS["bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"].replace(Tq=96, Tk=96)
+    q, k, v = (inputs.to_torch(x, "bf16") for x in inputs.make_inputs(cfg))
+    lse = torch.empty(cfg.B, cfg.Hq, cfg.Tq, dtype=torch.float32)
+    assert _bytes_of(q, k, v, torch.empty_like(q), lse) == \
+        acc.prefill_compulsory_bytes(2, 32, 8, 96, 96, 128)
+
+
+@pytest.mark.parametrize("Tq,Tk", [(1, 1), (7, 7), (64, 64), (5, 77), (300, 301)])
+def test_visible_pairs_by_brute_force_mask(Tq, Tk):
+    # count the entries a bottom-right causal mask keeps, with the mask built element by element
+    kept = sum(1 for i in range(Tq) for j in range(Tk) if j <= i + Tk - Tq)
+    assert acc.visible_pairs(Tq, Tk, True) == kept
+    assert acc.visible_pairs(Tq, Tk, False) == Tq * Tk
+    for W in (1, 3, 50):
+        kept_w = sum(1 for i in range(Tq) for j in range(Tk)
+                     if i + Tk - Tq - W < j <= i + Tk - Tq)
+        assert acc.visible_pairs(Tq, Tk, True, W) == kept_w
+
+
+@pytest.mark.parametrize("shape", [(1, 32, 8192, 128), (2, 32, 16384, 128), (4, 16, 1024, 64),
+                                   (1, 2, 5, 8)])
+def test_backward_flops_from_visible_pairs(shape):
+    # five products (S, dP, dV, dK, dQ), each one multiply-add of d terms per visible pair:
+    # 10 d FLOPs per pair. Without a mask every pair is visible; with it the causal-halved
+    # convention counts T^2 / 2 pairs against the T (T + 1) / 2 a square causal mask keeps.
+    import oracle
+
+    B, H, T, d = shape
+    pairs_full = B * H * T * T
+    assert oracle.backward_flops(B, H, T, T, d, False) == 10 * d * pairs_full
+    pairs_causal = B * H * acc.visible_pairs(T, T, True)
+    assert oracle.backward_flops(B, H, T, T, d, True) * (T + 1) == 10 * d * pairs_causal * T

@@ -61,12 +61,22 @@ def _np(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def nan_grads(q, k):
+    """dQ, dK, dV buffers filled with NaN: an element the kernels do not write fails the check."""
+    import torch
+
+    return (torch.full_like(q, float("nan")), torch.full_like(k, float("nan")),
+            torch.full_like(k, float("nan")))
+
+
 def run_bwd(fa, Q, K, V, O, L, dO, causal, scale, window=None):
     import torch
 
     lse = torch.from_numpy(np.ascontiguousarray(L, dtype=np.float32)).cuda()
-    dq, dk, dv = fa.attn_bwd(_dev(Q), _dev(K), _dev(V), _dev(inputs.round_to_bf16(O)), lse,
-                             _dev(dO), causal=causal, scale=scale, window=window)
+    q, k = _dev(Q), _dev(K)
+    dq, dk, dv = nan_grads(q, k)
+    fa.attn_bwd(q, k, _dev(V), _dev(inputs.round_to_bf16(O)), lse, _dev(dO), causal=causal,
+                scale=scale, window=window, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return _np(dq), _np(dk), _np(dv)
 
@@ -209,14 +219,23 @@ def test_end_to_end_small(fa):
         check_grad(_np(g), r, f"{cfg.name} {n}")
 
 
-def _sample(T, rng, n=24):
-    fixed = [0, 1, 31, 32, 127, 128, T // 2, T - 129, T - 33, T - 32, T - 2, T - 1]
-    return sorted({x for x in fixed + rng.choice(T, size=n, replace=False).tolist()
-                   if 0 <= x < T})
+def _sample(T, rng, n=24, lo=0):
+    """Sorted distinct indices in [lo, T): tile edges and the end, plus n drawn from the seed."""
+    fixed = [lo, lo + 1, lo + 31, lo + 32, lo + 127, lo + 128, (lo + T) // 2, T - 129, T - 33,
+             T - 32, T - 2, T - 1]
+    return sorted({x for x in fixed + (lo + rng.choice(T - lo, size=n, replace=False)).tolist()
+                   if lo <= x < T})
 
 
-def sampled_e2e(fa, cfg: AttnConfig, q_heads, kv_heads):
-    """Full-size forward then backward on the GPU; sampled dQ rows and dK/dV keys compared."""
+def sampled_e2e(fa, cfg: AttnConfig, late_keys=None, full_range_kv=None):
+    """Full-size forward then backward on the GPU into NaN-filled gradient buffers; every element
+    must be written and finite. Sampled dQ rows of every query head and sampled dK/dV keys of
+    every kv head are compared with the oracle.
+
+    The oracle's column form costs a whole forward per query head for keys near the start of the
+    sequence (every later row sees them). With ``late_keys`` set, kv heads other than those in
+    ``full_range_kv`` sample keys from the last ``late_keys`` positions only, which only the
+    rows after them see."""
     import torch
 
     _say(f"{cfg.name}: inputs")
@@ -225,44 +244,60 @@ def sampled_e2e(fa, cfg: AttnConfig, q_heads, kv_heads):
     q, k, v, do = _dev(Q), _dev(K), _dev(V), _dev(dO)
     _say(f"{cfg.name}: forward + backward")
     o, lse = fa.attn_fwd(q, k, v, causal=cfg.causal)
-    dq, dk, dv = fa.attn_bwd(q, k, v, o, lse, do, causal=cfg.causal)
+    dq, dk, dv = nan_grads(q, k)
+    fa.attn_bwd(q, k, v, o, lse, do, causal=cfg.causal, dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     for t in (dq, dk, dv):
         assert bool(torch.isfinite(t).all())
     del o, lse, q, k, v, do
     rng = np.random.default_rng(cfg.seed + 2000)
     G = cfg.group
-    for (b, h) in q_heads:
-        rows = _sample(cfg.Tq, rng)
-        _say(f"{cfg.name}: oracle dQ rows of ({b}, {h})")
-        ref = oracle.backward_rows(Q[b, h], K[b, h // G], V[b, h // G], dO[b, h], rows,
-                                   cfg.causal, cfg.scale)
-        check_grad(_np(dq[b, h, rows]), ref, f"{cfg.name} dQ ({b},{h})")
-    for (b, g) in kv_heads:
-        keys = _sample(cfg.Tk, rng)
-        rk = np.zeros((len(keys), cfg.d))
-        rv = np.zeros((len(keys), cfg.d))
-        for h in range(g * G, (g + 1) * G):
-            _say(f"{cfg.name}: oracle dK/dV keys of kv ({b}, {g}) from query head {h}")
-            sk, sv = oracle.backward_cols(Q[b, h], K[b, g], V[b, g], dO[b, h], keys, cfg.causal,
-                                          cfg.scale)
-            rk += sk
-            rv += sv
-        check_grad(_np(dk[b, g, keys]), rk, f"{cfg.name} dK ({b},{g})")
-        check_grad(_np(dv[b, g, keys]), rv, f"{cfg.name} dV ({b},{g})")
+    got_q, ref_q = [], []
+    _say(f"{cfg.name}: oracle dQ rows of all {cfg.B * cfg.Hq} query heads")
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            rows = _sample(cfg.Tq, rng)
+            ref_q.append(oracle.backward_rows(Q[b, h], K[b, h // G], V[b, h // G], dO[b, h], rows,
+                                              cfg.causal, cfg.scale))
+            got_q.append(_np(dq[b, h, rows]))
+    check_grad(np.concatenate(got_q), np.concatenate(ref_q), f"{cfg.name} dQ")
+    got_k, ref_k, got_v, ref_v = [], [], [], []
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            full = late_keys is None or (b, g) in (full_range_kv or [])
+            keys = _sample(cfg.Tk, rng, lo=0 if full else cfg.Tk - late_keys)
+            _say(f"{cfg.name}: oracle dK/dV of kv head ({b}, {g}), keys {keys[0]}..{keys[-1]}")
+            rk = np.zeros((len(keys), cfg.d))
+            rv = np.zeros((len(keys), cfg.d))
+            for h in range(g * G, (g + 1) * G):
+                sk, sv = oracle.backward_cols(Q[b, h], K[b, g], V[b, g], dO[b, h], keys,
+                                              cfg.causal, cfg.scale)
+                rk += sk
+                rv += sv
+            got_k.append(_np(dk[b, g, keys]))
+            got_v.append(_np(dv[b, g, keys]))
+            ref_k.append(rk)
+            ref_v.append(rv)
+            check_grad(got_k[-1], rk, f"{cfg.name} dK ({b},{g})")
+            check_grad(got_v[-1], rv, f"{cfg.name} dV ({b},{g})")
+    check_grad(np.concatenate(got_k), np.concatenate(ref_k), f"{cfg.name} dK")
+    check_grad(np.concatenate(got_v), np.concatenate(ref_v), f"{cfg.name} dV")
 
 
-def test_causal_t8192_d128_sampled(fa):
-    # B=1, H=32, T=8192, d=128, causal: the forward's headline shape.
-    sampled_e2e(fa, inputs.CONFIGS["bf16_causal_b1_h32_t8192_d128"], [(0, 0), (0, 31)], [(0, 7)])
+def test_causal_t8192_d128_every_head_sampled(fa):
+    # B=1, H=32, T=8192, d=128, causal: the forward's headline shape; sampled rows and keys of
+    # every head, keys over the whole sequence
+    sampled_e2e(fa, inputs.CONFIGS["bf16_causal_b1_h32_t8192_d128"])
 
 
-def test_noncausal_t8000_d128_sampled(fa):
+def test_noncausal_t8000_d128_every_head_sampled(fa):
     cfg = inputs.CONFIGS["bf16_causal_b1_h32_t8000_d128"].replace(causal=False, name="noncausal t8000")
-    sampled_e2e(fa, cfg, [(0, 5)], [(0, 20)])
+    sampled_e2e(fa, cfg)
 
 
-def test_gqa_causal_t16384_d128_sampled(fa):
+def test_gqa_causal_t16384_d128_every_head_sampled(fa):
     # B=2, Hq=32, Hkv=8, T=16384, d=128, causal, 1% of K rows x8: a kv head's gradient sums
-    # four query heads.
-    sampled_e2e(fa, inputs.CONFIGS["bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"], [(1, 17)], [(0, 3)])
+    # four query heads. dQ rows of all 64 query heads; dK/dV keys of all 16 kv heads, over the
+    # whole sequence for two of them and from the last 1024 positions for the rest.
+    sampled_e2e(fa, inputs.CONFIGS["bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"], late_keys=1024,
+                full_range_kv=[(0, 3), (1, 6)])

@@ -4,10 +4,11 @@ Bounds (on both O and LSE): fp32 inputs, max abs error <= 1e-5; bf16 inputs, max
 <= 2e-2 and mean-relative error sum|gpu - ref| / sum|ref| <= 1e-2. The oracle reads the same
 rounded input values widened exactly to float64.
 
-Small problems are compared in full (several tiles, ragged tails, every launch configuration);
-the five full-size workloads run at their real shape in the default configuration and are
-compared on sampled rows that the oracle computes one by one, plus a whole-tensor finiteness
-check.
+Small problems are compared in full (several tiles, ragged tails, every launch configuration).
+The five full-size workloads run at their real shape in the default configuration, into
+NaN-filled output buffers: the fp32 T=128, bf16 T=1024, the T=8192 causal prefill and its three
+variants and the GQA decode are compared on every element; the GQA T=16384 prefill on sampled
+rows of every one of its 64 heads, which the oracle computes one by one.
 """
 
 import math
@@ -46,10 +47,16 @@ def _to_dev(x, dtype):
 
 
 def run_gpu(fa, Q, K, V, causal, scale, dtype, cfg=None):
+    """One call through the C ABI into NaN-filled O and LSE buffers (an element the kernels do
+    not write stays NaN and fails the comparison)."""
     import torch
 
-    o, lse = fa.attn_fwd(_to_dev(Q, dtype), _to_dev(K, dtype), _to_dev(V, dtype), causal=causal,
-                         scale=scale, cfg=cfg)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, Hq, Tq, d = Q.shape
+    o = torch.full((B, Hq, Tq, d), float("nan"), dtype=tdt, device="cuda")
+    lse = torch.full((B, Hq, Tq), float("nan"), dtype=torch.float32, device="cuda")
+    fa.attn_fwd(_to_dev(Q, dtype), _to_dev(K, dtype), _to_dev(V, dtype), causal=causal,
+                scale=scale, cfg=cfg, out=o, lse=lse)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
@@ -254,19 +261,55 @@ def _sample_rows(T, rng, n=48):
     return sorted({r for r in fixed + rnd if 0 <= r < T})
 
 
-def sampled_case(fa, cfg: AttnConfig, heads):
-    """Run the whole workload on the GPU; compare sampled rows of the given (b, h) heads."""
+def nan_outputs(cfg: AttnConfig, dtype):
+    """O and LSE buffers filled with NaN, so that any element the kernels leave unwritten fails
+    the comparison (and the finiteness check) instead of passing on leftover memory."""
+    import torch
+
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o = torch.full((cfg.B, cfg.Hq, cfg.Tq, cfg.d), float("nan"), dtype=tdt, device="cuda")
+    lse = torch.full((cfg.B, cfg.Hq, cfg.Tq), float("nan"), dtype=torch.float32, device="cuda")
+    return o, lse
+
+
+def whole_case(fa, cfg: AttnConfig):
+    """Run the whole workload on the GPU into NaN-filled buffers and compare every element of O
+    and LSE with the oracle; the mean-relative bound is taken over the whole tensor."""
     import torch
 
     _say(f"{cfg.name}: generating inputs")
     Q, K, V = inputs.make_inputs(cfg)
     q, k, v = (_to_dev(x, cfg.dtype) for x in (Q, K, V))
+    o, lse = nan_outputs(cfg, cfg.dtype)
     _say(f"{cfg.name}: launching")
-    o, l = fa.attn_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale)
+    fa.attn_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    og = o.float().cpu().numpy().astype(np.float64)
+    lg = lse.cpu().numpy().astype(np.float64)
+    del q, k, v, o, lse
+    _say(f"{cfg.name}: oracle on every head")
+    o_ref, l_ref = oracle.dense_attention(Q, K, V, cfg.causal, cfg.scale)
+    check(og, lg, o_ref, l_ref, cfg.dtype, cfg.name)
+
+
+def sampled_case(fa, cfg: AttnConfig, heads=None):
+    """Run the whole workload on the GPU into NaN-filled buffers; check that every element was
+    written and is finite, and compare sampled rows of the given (b, h) heads (default: every
+    head, with its own row sample) with the oracle, the mean-relative bound over all of them."""
+    import torch
+
+    _say(f"{cfg.name}: generating inputs")
+    Q, K, V = inputs.make_inputs(cfg)
+    q, k, v = (_to_dev(x, cfg.dtype) for x in (Q, K, V))
+    o, l = nan_outputs(cfg, cfg.dtype)
+    _say(f"{cfg.name}: launching")
+    fa.attn_fwd(q, k, v, causal=cfg.causal, scale=cfg.scale, out=o, lse=l)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(l).all())
+    if heads is None:
+        heads = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
     rng = np.random.default_rng(cfg.seed + 1000)
-    _say(f"{cfg.name}: oracle on sampled rows")
+    _say(f"{cfg.name}: oracle on sampled rows of {len(heads)} heads")
     og, lg, orf, lrf = [], [], [], []
     for (b, h) in heads:
         g = h // cfg.group
@@ -291,14 +334,15 @@ def test_bf16_causal_t1024_d64_full(fa):
 
 @pytest.mark.parametrize("name", ["bf16_causal_b1_h32_t8192_d128", "bf16_noncausal_b1_h32_t4096_d128",
                                   "bf16_causal_b1_h32_t8000_d128"])
-def test_bf16_t8192_shapes_sampled(fa, name):
-    cfg = inputs.CONFIGS[name]
-    sampled_case(fa, cfg, heads=[(0, 0), (0, 13), (0, 31)])
+def test_bf16_t8192_shapes_whole(fa, name):
+    # B=1, H=32, d=128: causal T=8192, its non-causal T=4096 variant and the ragged causal
+    # T=8000, every element of O and LSE against the oracle
+    whole_case(fa, inputs.CONFIGS[name])
 
 
-def test_bf16_noncausal_t8000_sampled(fa):
+def test_bf16_noncausal_t8000_whole(fa):
     cfg = inputs.CONFIGS["bf16_causal_b1_h32_t8000_d128"].replace(causal=False, name="noncausal t8000")
-    sampled_case(fa, cfg, heads=[(0, 5)])
+    whole_case(fa, cfg)
 
 
 def test_gqa_decode_full(fa):
@@ -321,6 +365,7 @@ def test_gqa_decode_full(fa):
     check(o, l, o_ref, l_ref, cfg.dtype, cfg.name)
 
 
-def test_gqa_causal_t16384_sampled(fa):
-    cfg = inputs.CONFIGS["bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"]
-    sampled_case(fa, cfg, heads=[(0, 0), (0, 3), (1, 17), (1, 31)])
+def test_gqa_causal_t16384_every_head_sampled(fa):
+    # B=2, Hq=32, Hkv=8, T=16384: all 64 heads written (NaN-filled buffers), 66 sampled rows of
+    # every head against the oracle
+    sampled_case(fa, inputs.CONFIGS["bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"])

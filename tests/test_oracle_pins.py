@@ -136,7 +136,7 @@ def test_online_weighted_sum_against_library_softmax():
     V = rng.normal(0, 1, size=(37, 8))
     ref = softmax(x) @ V
     for bs in (1, 4, 5, 37, 64):
-        assert np.max(np.abs(oracle.online_softmax_weighted_sum(x, V, bs) - ref)) < 1e-14
+        assert np.max(np.abs(oracle.stream_weighted_sum(x, V, bs) - ref)) < 1e-14
 
 
 @pytest.mark.parametrize("chunk", [1, 3, 16, 100])
@@ -145,7 +145,7 @@ def test_online_softmax_against_torch_softmax(chunk):
 
     x = np.random.default_rng(3).normal(0, 20, size=100)   # scores scaled up to stress the max
     ref = torch.softmax(torch.from_numpy(x), dim=0).numpy()
-    assert np.max(np.abs(oracle.online_softmax(x, chunk) - ref)) < 1e-15
+    assert np.max(np.abs(oracle.stream_softmax(x, chunk) - ref)) < 1e-15
 
 
 # ---------------------------------------------------------------- closed forms and invariants
