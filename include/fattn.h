@@ -55,7 +55,9 @@ typedef struct fattn_cfg {
   int block_kv; /* keys per tile (prefill MFMA: 32 or 64; decode: 32) */
   int waves;    /* wavefronts (64 lanes) per workgroup */
   int splits;   /* decode: key-range splits per (batch, kv head) */
-  int schedule; /* prefill grid order: 1 = row-major, 2 = XCD-grouped, longest causal first */
+  int schedule; /* prefill grid order: 1 = row-major, 2 = XCD-grouped, longest causal first,
+                   4 = one workgroup per pair of query blocks of a (batch, head), the longer
+                   causal block first (dense batches, 8 waves only) */
 } fattn_cfg_t;
 
 /*

@@ -107,7 +107,8 @@ int make_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int dty
       }
       if (p.block_kv != 32 && p.block_kv != 64) return FATTN_ERR_UNSUPPORTED;
       if (p.waves != 4 && p.waves != 8) return FATTN_ERR_UNSUPPORTED;
-      if (p.schedule != 1 && p.schedule != 2) return FATTN_ERR_UNSUPPORTED;
+      if (p.schedule != 1 && p.schedule != 2 && p.schedule != 4) return FATTN_ERR_UNSUPPORTED;
+      if (p.schedule == 4 && p.waves != 8) return FATTN_ERR_UNSUPPORTED;
       p.block_q = 32 * p.waves;
       if (cfg && cfg->block_q && cfg->block_q != p.block_q) return FATTN_ERR_UNSUPPORTED;
       break;

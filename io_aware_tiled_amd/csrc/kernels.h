@@ -27,7 +27,8 @@ struct Problem {
 
 // bf16 matrix-core prefill. block_kv in {32, 64}, waves in {4, 8}, d in {32, 64, 128};
 // schedule 1 = row-major grid, 2 = whole heads per XCD, 8 heads at a time query-block-major with
-// the longest causal blocks first (grid_order.h).
+// the longest causal blocks first (grid_order.h), 4 = one workgroup per pair of blocks of a
+// (batch, head), block nqb-1-p then block p, pairs dealt to the XCDs in contiguous ranges.
 hipError_t launch_prefill_bf16(const Problem& p, int block_kv, int waves, int schedule,
                                hipStream_t stream);
 

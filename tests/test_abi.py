@@ -103,7 +103,9 @@ def test_empty_problems_are_noops(kw):
 
 
 @pytest.mark.parametrize("cfg", [dict(block_kv=48), dict(waves=2), dict(waves=16),
-                                 dict(schedule=9), dict(kernel=99), dict(kernel=3),
+                                 dict(schedule=9), dict(schedule=3), dict(schedule=4, waves=4),
+                                 dict(kernel=99),
+                                 dict(kernel=3),
                                  dict(kernel=2), dict(splits=4), dict(block_q=64)])
 def test_unsupported_configs(cfg):
     assert fa.lib.attn_fwd_plan(1, 8, 2, 64, 64, 64, 1, BF16, ctypes.byref(fa._make_cfg(cfg)),

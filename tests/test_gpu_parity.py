@@ -97,8 +97,9 @@ def _small(name, B, Hq, Hkv, Tq, Tk, d, dtype="bf16", causal=True, dist="normal"
 
 # ------------------------------------------------------------------ small problems, in full
 
+# schedule 1: row-major grid; 2: XCD-grouped, longest causal blocks first; 4: paired blocks
 PREFILL_LAUNCHES = [dict(block_kv=bc, waves=nw, schedule=sch)
-                    for bc in (32, 64) for nw in (4, 8) for sch in (1, 2)]
+                    for bc in (32, 64) for nw in (4, 8) for sch in (1, 2, 4) if sch != 4 or nw == 8]
 
 
 @pytest.mark.parametrize("launch", PREFILL_LAUNCHES, ids=lambda c: "bc{block_kv}_w{waves}_s{schedule}".format(**c))
@@ -112,6 +113,23 @@ def test_prefill_bf16_every_launch_config(fa, d, launch):
                          causal=causal, seed=d + Tq)
             _say(f"{cfg.name} {launch}")
             full_case(fa, cfg, dict(launch, kernel=fa.FATTN_KERNEL_PREFILL_MFMA))
+
+
+@pytest.mark.parametrize("launch", [dict(block_kv=bc, waves=8) for bc in (32, 64)],
+                         ids=lambda c: "bc{block_kv}_w{waves}".format(**c))
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_paired_blocks(fa, d, launch):
+    # Schedule 4 runs query blocks nqb-1-p and p of a (batch, head) in one workgroup, the second
+    # with its Q prefetched into LDS and its first K and V tiles issued early. Block counts here
+    # are even and odd (an odd count leaves the middle block alone in its workgroup), the last
+    # block is ragged, and GQA groups differ.
+    cases = [(True, 2, 16, 4, 4100), (False, 4, 16, 16, 2100), (True, 2, 16, 2, 1500),
+             (True, 1, 4, 1, 300), (False, 3, 2, 2, 129)]
+    for causal, B, Hq, Hkv, T in cases:
+        cfg = _small(f"paired d{d} B{B} Hq{Hq} Hkv{Hkv} T{T} c{int(causal)}", B, Hq, Hkv, T, T, d,
+                     causal=causal, seed=d + T)
+        _say(f"{cfg.name} {launch}")
+        full_case(fa, cfg, dict(launch, kernel=fa.FATTN_KERNEL_PREFILL_MFMA, schedule=4))
 
 
 @pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 513])

@@ -54,7 +54,7 @@ def window_case(fa, cfg, W, launch=None):
 
 
 PREFILL_LAUNCHES = [dict(kernel=1, block_kv=bc, waves=nw, schedule=sch)
-                    for bc in (32, 64) for nw in (4, 8) for sch in (1, 2)]
+                    for bc in (32, 64) for nw in (4, 8) for sch in (1, 2, 4) if sch != 4 or nw == 8]
 
 
 @pytest.mark.parametrize("launch", PREFILL_LAUNCHES,
