@@ -103,6 +103,22 @@ int attn_fwd_cfg(const void* Q, const void* K, const void* V, void* O, float* LS
                  const fattn_cfg_t* cfg);
 
 /*
+ * attn_fwd_noalloc: attn_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. Same arguments, layouts,
+ * results and error codes as attn_fwd, and it calls no hipMalloc, hipFree or other allocating
+ * routine. The split-K decode (Tq == 1, bf16) keeps its per-split partial outputs in a static
+ * device array of 16 MiB (4 * 2^20 floats) that each GPU holds from library load until the
+ * process ends, instead of attn_fwd's grow-only workspace; the split count is lowered where
+ * needed so that splits * B * Hq * (d + 1) floats fit, and a shape with B * Hq * (d + 1) above
+ * 4 * 2^20 is rejected with FATTN_ERR_INVALID before any HIP call. Every call on one GPU shares
+ * that array, so calls that overlap on one GPU (different streams or threads) race: serialise
+ * them. The prefill paths use no scratch memory and run as in attn_fwd.
+ */
+int attn_fwd_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                     int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale, int dtype,
+                     void* stream);
+
+/*
  * attn_fwd_plan: host-only query of the configuration attn_fwd would launch for this shape
  * (after validation, with `cfg` overrides applied when non-NULL); writes it to *out.
  * Same return codes as attn_fwd; makes no HIP call.

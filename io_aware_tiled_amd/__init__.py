@@ -70,6 +70,8 @@ lib.attn_fwd.argtypes = _FWD_ARGS
 lib.attn_fwd.restype = _i
 lib.attn_fwd_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]
 lib.attn_fwd_cfg.restype = _i
+lib.attn_fwd_noalloc.argtypes = _FWD_ARGS
+lib.attn_fwd_noalloc.restype = _i
 lib.attn_fwd_window.argtypes = _FWD_ARGS
 lib.attn_fwd_window.restype = _i
 lib.attn_fwd_window_cfg.argtypes = _FWD_ARGS + [ctypes.POINTER(FattnCfg)]

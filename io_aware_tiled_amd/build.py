@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libfattn.so")
 
-SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip", "backward_bf16.hip"]
+SOURCES = ["api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode_bf16.hip", "backward_bf16.hip",
+           "noalloc.hip"]
 PROBE_SOURCES = ["probe.hip"]
 PROBE_LIB_PATH = os.path.join(HERE, "libfattn_probe.so")
 

@@ -213,9 +213,11 @@ namespace {
 
 // The forward pass behind every entry point. window == 0: no window; window >= 1: sliding
 // window, causal implied (checked by the callers).
+// noalloc: the split-K decode uses the static scratch (noalloc.hip) instead of the workspace,
+// with its split count capped to fit; nothing is allocated.
 int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int Hq,
             int Hkv, int Tq, int Tk, int d, int causal, int window, float scale, int dtype,
-            void* stream, const fattn_cfg_t* cfg) {
+            void* stream, const fattn_cfg_t* cfg, bool noalloc = false) {
   bool noop;
   int rc = validate_shape(B, Hq, Hkv, Tq, Tk, d, causal, dtype, &noop);
   if (rc != FATTN_OK) return rc;
@@ -232,6 +234,22 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   fattn_cfg_t plan;
   rc = make_plan(B, Hq, Hkv, Tq, Tk - k0, d, causal, dtype, cfg, &plan);
   if (rc != FATTN_OK) return fail(rc, "launch configuration not implemented for this shape");
+  if (noalloc && plan.kernel == FATTN_KERNEL_DECODE_SPLITK) {
+    // the partials of every split must fit the static scratch: fewer splits if needed
+    const size_t per_split = (size_t)B * Hq * (size_t)(d + 1);
+    const size_t fit = kScratchFloats / per_split;
+    if (fit < 1)
+      return fail(FATTN_ERR_INVALID,
+                  "B*Hq*(d+1) = %zu floats exceeds the static scratch of %zu floats", per_split,
+                  kScratchFloats);
+    if ((size_t)plan.splits > fit) {
+      fattn_cfg_t c = cfg ? *cfg : fattn_cfg_t{};
+      c.kernel = FATTN_KERNEL_DECODE_SPLITK;
+      c.splits = (int)fit;
+      rc = make_plan(B, Hq, Hkv, Tq, Tk - k0, d, causal, dtype, &c, &plan);
+      if (rc != FATTN_OK) return fail(rc, "launch configuration not implemented for this shape");
+    }
+  }
 
   Problem p;
   p.Q = Q;
@@ -268,8 +286,14 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
       const int chunk = ((nkeys + plan.splits - 1) / plan.splits + 31) / 32 * 32;
       const size_t rows = (size_t)B * Hq * plan.splits;
       const size_t need = rows * (size_t)d + rows;
-      std::lock_guard<std::mutex> lock(g_ws_mutex);
       float* ws = nullptr;
+      if (noalloc) {
+        he = static_scratch(dev, &ws);
+        if (he != hipSuccess) return hip_fail(FATTN_ERR_HIP, "hipGetSymbolAddress", he);
+        e = launch_decode_bf16(p, k0, plan.splits, chunk, ws, ws + rows * (size_t)d, s);
+        break;
+      }
+      std::lock_guard<std::mutex> lock(g_ws_mutex);
       rc = workspace(dev, s, need, &ws);
       if (rc != FATTN_OK) return rc;
       e = launch_decode_bf16(p, k0, plan.splits, chunk, ws, ws + rows * (size_t)d, s);
@@ -296,6 +320,14 @@ extern "C" int attn_fwd(const void* Q, const void* K, const void* V, void* O, fl
                         void* stream) {
   return attn_fwd_cfg(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, stream,
                       nullptr);
+}
+
+extern "C" int attn_fwd_noalloc(const void* Q, const void* K, const void* V, void* O,
+                                float* LSE, int B, int Hq, int Hkv, int Tq, int Tk, int d,
+                                int causal, float scale, int dtype, void* stream) {
+  g_last_error[0] = 0;
+  return forward(Q, K, V, O, LSE, B, Hq, Hkv, Tq, Tk, d, causal, 0, scale, dtype, stream,
+                 nullptr, true);
 }
 
 extern "C" int attn_fwd_window_cfg(const void* Q, const void* K, const void* V, void* O,

@@ -93,6 +93,12 @@ struct BwdProblem {
   float scale;  // signed softmax scale
 };
 
+// Static scratch of the entry point that allocates nothing: kScratchFloats floats per device,
+// a file-scope device array (noalloc.hip). static_scratch returns its device address on device
+// `dev`, which must be current; the first call per device looks it up, later calls return it.
+constexpr size_t kScratchFloats = size_t(4) << 20;  // 16 MiB
+hipError_t static_scratch(int dev, float** out);
+
 // Floats of backward workspace: (L, D) in 32-row blocks for every (batch, query head).
 inline size_t backward_workspace_floats(int B, int Hq, int Tq) {
   return (size_t)B * Hq * (size_t)((Tq + 31) / 32) * 64;
