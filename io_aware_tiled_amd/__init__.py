@@ -17,7 +17,8 @@ import re
 from typing import Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfattn.so")
+# FATTN_LIB names another build of the same library (the tests' host-only sanitizer build)
+LIB_PATH = os.environ.get("FATTN_LIB") or os.path.join(_HERE, "libfattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fattn.h")
 
 if not os.path.exists(LIB_PATH):
