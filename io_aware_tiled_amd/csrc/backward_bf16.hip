@@ -14,7 +14,8 @@
 //  * bwd_dq_kernel (query-block outer loop, like the forward): a lane owns a query row and
 //    streams the K and V tiles of its head; per tile S^T and dP^T come from two MFMA products
 //    against Q^T and dO^T held in registers, dS is formed on the VALU, and dQ^T += K^T dS^T
-//    reads the same K tile transposed.
+//    reads the same K tile transposed. Software-pipelined like the forward: the products of the
+//    next tile are issued together with the current tile's exponentials.
 //  * bwd_dkdv_kernel (key-block outer loop): a lane owns a key and holds V^T in registers; at
 //    d = 128 the workgroup's K rows sit in LDS for its whole life (read as the K^T operand), which
 //    keeps the kernel within 256 registers and so at two waves per SIMD (K^T stays in registers
@@ -168,7 +169,10 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     int Hkv, int Tq, int Tk, int causal, int window, float scale, float c,
     const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
   using S = Shape<D, BC, NW>;
+  // One array per stage (K rotates through four, V through two; see the pipeline below), so
+  // the compiler can tell a direct-to-LDS load into one stage from reads of another.
   __shared__ __align__(1024) unsigned char k_st0[S::TILE], k_st1[S::TILE];
+  __shared__ __align__(1024) unsigned char k_st2[S::TILE], k_st3[S::TILE];
   __shared__ __align__(1024) unsigned char v_st0[S::TILE], v_st1[S::TILE];
 
   const int tid = threadIdx.x;
@@ -298,39 +302,38 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
            (window == 0 || (j + 1) * BC - 1 >= qw0 + off - window + 1);
   };
 
-  auto compute = [&](int j, const unsigned char* kst, const unsigned char* vst) {
-    f32x16 s[BC / 32], dp[BC / 32];
+  // S^T and dP^T of one key tile from its K and V stages
+  auto sdp = [&](f32x16 (&s)[BC / 32], f32x16 (&dp)[BC / 32], const unsigned char* kst,
+                 const unsigned char* vst) {
     rows_x(s, kst, qb8);
     rows_x(dp, vst, ob8);
-    bf16x8 ds[BC / 16];
+  };
+  // dS of key tile j, rounded to bf16. Two copies of the element loop, with and without the
+  // mask, so that neither holds a branch.
+  auto dsoft = [&](int j, const f32x16 (&s)[BC / 32], const f32x16 (&dp)[BC / 32],
+                   bf16x8 (&ds)[BC / 16], auto with_mask) {
     // visible keys of the tile for this lane's row (relative to the tile start): key_lo..key_hi
     const int j0 = j * BC;
     const int key_hi = (causal ? min(Tk - 1, qrow + off) : Tk - 1) - j0;
     const int key_lo = (window > 0 ? qrow + off - window + 1 : 0) - j0;
-    // two copies of the element loop, with and without the mask, so neither holds a branch
-    auto elements = [&](auto with_mask) {
 #pragma unroll
-      for (int ch = 0; ch < BC / 16; ++ch) {
-        const int t = ch >> 1, c2 = ch & 1;
+    for (int ch = 0; ch < BC / 16; ++ch) {
+      const int t = ch >> 1, c2 = ch & 1;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = 8 * c2 + i;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -Lr));
-          float v = p * (dp[t][r] - Dr);
-          if constexpr (decltype(with_mask)::value) {
-            const int kk = 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-            v = (kk > key_hi || kk < key_lo) ? 0.f : v;
-          }
-          ds[ch][i] = (__bf16)v;
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * c2 + i;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], c, -Lr));
+        float v = p * (dp[t][r] - Dr);
+        if constexpr (decltype(with_mask)::value) {
+          const int kk = 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+          v = (kk > key_hi || kk < key_lo) ? 0.f : v;
         }
+        ds[ch][i] = (__bf16)v;
       }
-    };
-    if (!clean(j)) {
-      elements(std::true_type{});
-    } else {
-      elements(std::false_type{});
     }
-    // dQ^T += K^T dS^T: the K tile read transposed
+  };
+  // dQ^T += K^T dS^T: the K stage of the tile read transposed
+  auto dq = [&](const bf16x8 (&ds)[BC / 16], const unsigned char* kst) {
 #pragma unroll
     for (int ch = 0; ch < BC / 16; ++ch)
 #pragma unroll
@@ -345,38 +348,93 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
       }
   };
 
+  // Software pipeline over the key tiles: the step of tile j forms S^T and dP^T of tile j+1
+  // (matrix cores) while it forms dS of tile j (VALU), then adds K^T dS^T of tile j, and loads
+  // the K and V tiles of j+2. Tile j's K stage is still read (transposed) while tile j+2 loads,
+  // so K rotates through four stages (three would do; four keep the rotation in step with the
+  // two V stages and the two score buffers, so the unrolled steady state names every buffer
+  // statically); V's stage of tile j is free once S^T and dP^T of tile j were formed a step
+  // earlier, so V needs two.
+  auto kst = [&](int i) { return i == 0 ? k_st0 : i == 1 ? k_st1 : i == 2 ? k_st2 : k_st3; };
+  auto vst = [&](int i) { return i == 0 ? v_st0 : v_st1; };
+
   // Stages start cleared: a stage row past Tk is then zero or a finite leftover of an earlier
   // tile, and meets a zero dS.
   for (int i = tid; i < S::TILE / 16; i += S::NT) {
-    *(LDS_AS u32x4*)(k_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-    *(LDS_AS u32x4*)(k_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *(LDS_AS u32x4*)(kst(k) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
     *(LDS_AS u32x4*)(v_st0 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
     *(LDS_AS u32x4*)(v_st1 + 16 * i) = u32x4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
+  // prologue: tiles j_lo and j_lo+1 in stages 0 and 1; S^T and dP^T of tile j_lo
   if (j_lo < ntiles) {
     load_tile(Kh, j_lo * BC, k_st0);
     load_tile(Vh, j_lo * BC, v_st0);
   }
+  if (j_lo + 1 < ntiles) {
+    load_tile(Kh, (j_lo + 1) * BC, k_st1);
+    load_tile(Vh, (j_lo + 1) * BC, v_st1);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  f32x16 sa[BC / 32], pa[BC / 32], sb[BC / 32], pb[BC / 32];
+  if (j_lo < ntiles && active(j_lo)) sdp(sa, pa, k_st0, v_st0);
+  __syncthreads();  // V stage 0 is free for tile j_lo + 2
 
-  auto step = [&](int j, const unsigned char* k_cur, const unsigned char* v_cur,
-                  unsigned char* k_nxt, unsigned char* v_nxt) {
-    if (j + 1 < ntiles) {
-      load_tile(Kh, (j + 1) * BC, k_nxt);
-      load_tile(Vh, (j + 1) * BC, v_nxt);
-    }
-    if (active(j)) compute(j, k_cur, v_cur);
+  // steady state: tiles j, j+1 and j+2 are clean (every wave active, no mask)
+  auto fast_step = [&](f32x16 (&sc)[BC / 32], f32x16 (&pc)[BC / 32], f32x16 (&sn)[BC / 32],
+                       f32x16 (&pn)[BC / 32], int j, const unsigned char* k_cur,
+                       const unsigned char* k_nxt, unsigned char* k_far,
+                       const unsigned char* v_nxt, unsigned char* v_far) {
+    load_tile(Kh, (j + 2) * BC, k_far);
+    load_tile(Vh, (j + 2) * BC, v_far);
+    bf16x8 ds[BC / 16];
+    sdp(sn, pn, k_nxt, v_nxt);
+    dsoft(j, sc, pc, ds, std::false_type{});
+    dq(ds, k_cur);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
+  // general step: masks, inactive waves, the window's left band and the end of the pipeline
+  auto general_step = [&](int j) {
+    const int u = j - j_lo;
+    const unsigned char* k_cur = kst(u & 3);
+    const unsigned char* k_nxt = kst((u + 1) & 3);
+    const unsigned char* v_nxt = vst((u + 1) & 1);
+    if (j + 2 < ntiles) {
+      load_tile(Kh, (j + 2) * BC, kst((u + 2) & 3));
+      load_tile(Vh, (j + 2) * BC, vst(u & 1));
+    }
+    if (j + 1 < ntiles && active(j + 1)) sdp(sb, pb, k_nxt, v_nxt);
+    if (active(j)) {
+      bf16x8 ds[BC / 16];
+      if (clean(j)) {
+        dsoft(j, sa, pa, ds, std::false_type{});
+      } else {
+        dsoft(j, sa, pa, ds, std::true_type{});
+      }
+      dq(ds, k_cur);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < BC / 32; ++t) {
+      sa[t] = sb[t];
+      pa[t] = pb[t];
+    }
+  };
+  // left band of a window and the steps up to a multiple of four from j_lo, then the steady
+  // state over clean tiles, then the rest
   int j = j_lo;
-  for (; j + 1 < ntiles; j += 2) {
-    step(j, k_st0, v_st0, k_st1, v_st1);
-    step(j + 1, k_st1, v_st1, k_st0, v_st0);
+  for (; j < ntiles && (j < j_ul || ((j - j_lo) & 3) != 0); ++j) general_step(j);
+  for (; j + 5 < jm; j += 4) {
+    fast_step(sa, pa, sb, pb, j, k_st0, k_st1, k_st2, v_st1, v_st0);
+    fast_step(sb, pb, sa, pa, j + 1, k_st1, k_st2, k_st3, v_st0, v_st1);
+    fast_step(sa, pa, sb, pb, j + 2, k_st2, k_st3, k_st0, v_st1, v_st0);
+    fast_step(sb, pb, sa, pa, j + 3, k_st3, k_st0, k_st1, v_st0, v_st1);
   }
-  if (j < ntiles) step(j, k_st0, v_st0, k_st1, v_st1);
+  for (; j < ntiles; ++j) general_step(j);
 
   // rows qw0 .. qw0+31 of this head (packed batches keep Hq * D elements between rows)
   __bf16* rows = VARLEN ? dQ + ((size_t)(q_begin + qw0) * Hq + h) * D
