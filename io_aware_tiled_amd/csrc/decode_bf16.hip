@@ -38,7 +38,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr int KB = 32;       // keys per block
-constexpr int VS = KB + 8;   // LDS row pitch of V^T (elements): +16 bytes
+
+// LDS layouts of the per-wave K rows and V^T block. Measured on gfx950 with a probe of the
+// counter SQ_LDS_BANK_CONFLICT: a 16-byte LDS read (ds_read_b128) is served in four passes of 16
+// lanes, each pass one half of the wave (lanes 0-31 or 32-63) and, within it, the 4-lane quads
+// whose index has even (or odd) parity, against 64 four-byte banks; a 16-byte write
+// (ds_write_b128) in passes of 8 consecutive lanes against 32 banks. The element offsets below
+// give every pass of the kernel's reads and writes distinct banks.
+//
+// K: key row r (D elements, no padding), logical 16-byte chunk c stored at chunk c ^ f(r).
+template <int D>
+__device__ __forceinline__ int k_at(int r, int c) {
+  const int f = D >= 64 ? r % (D / 8) : ((r >> 3) & 1) << 1;
+  return r * D + 8 * (c ^ f);
+}
+// V^T: dim row r of 32 keys (4 chunks), rows 8 apart in the writes moved to the other half of
+// the 32 banks (r ^ bit 3 of r), chunks of odd rows swapped in pairs for the reads.
+__device__ __forceinline__ int vt_at(int r, int c) {
+  return (r ^ ((r >> 3) & 1)) * KB + 8 * (c ^ ((r & 1) << 1));
+}
 
 __device__ __forceinline__ uint32_t pick_half(uint32_t a, uint32_t b, int hi) {
   return hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
@@ -51,7 +69,6 @@ struct Block {
   u32x4 k[2][D / 32];
   u32x4 v[8];          // V rows of keys 4gg+r and 16+4gg+r, dims 8dg .. 8dg+8
 };
-constexpr int kPad = 8;  // LDS row pitch of K: D + 8 elements (16 bytes apart in the banks)
 
 // Where the 16-key halves of a 32-key block live. Keys kb + 16h + r (r < 16) are rows
 // row[h] + r of the K and V bases; a half whose rows are not readable has ok[h] false.
@@ -137,8 +154,8 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
     float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hq, int Hkv, int Tk, int k0,
     int splits, int chunk, float log2_scale, int qsign, const int* __restrict__ table,
     const int* __restrict__ seq_lens, int max_blocks, int bs_shift, int nblocks) {
-  __shared__ __align__(16) __bf16 Vt[D * VS];
-  __shared__ __align__(16) __bf16 Kt[KB * (D + kPad)];
+  __shared__ __align__(16) __bf16 Vt[D * KB];
+  __shared__ __align__(16) __bf16 Kt[KB * D];
 
   const int lane = threadIdx.x;
   const int c16 = lane & 15, g4 = lane >> 4;
@@ -205,7 +222,7 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
                      pick_half(cur.v[2][wd], cur.v[3][wd], hi),
                      pick_half(cur.v[4][wd], cur.v[5][wd], hi),
                      pick_half(cur.v[6][wd], cur.v[7][wd], hi)};
-        *reinterpret_cast<u32x4*>(Vt + (8 * dg + e) * VS + 8 * gg) = row;
+        *reinterpret_cast<u32x4*>(Vt + vt_at(8 * dg + e, gg)) = row;
       }
     }
 
@@ -215,8 +232,8 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
-          *reinterpret_cast<u32x4*>(Kt + (16 * t + c * RPI + lane / CPR) * (D + kPad) +
-                                    8 * (lane % CPR)) = cur.k[t][c];
+          *reinterpret_cast<u32x4*>(Kt + k_at<D>(16 * t + c * RPI + lane / CPR, lane % CPR)) =
+              cur.k[t][c];
     }
     __syncthreads();  // K rows of this block are in LDS
 
@@ -227,8 +244,8 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
       st[t] = f32x4{};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + (16 * t + c16) * (D + kPad) +
-                                                          32 * c + 8 * g4);
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(Kt + k_at<D>(16 * t + c16, 4 * c + g4));
         st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[c], st[t], 0, 0, 0);
       }
     }
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(64, 2) void decode_partial_kernel(
     __syncthreads();  // V^T of this block is in LDS
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + (16 * mt + c16) * VS + 8 * g4);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + vt_at(16 * mt + c16, g4));
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, acc[mt], 0, 0, 0);
     }
     if (more) cur = nxt;

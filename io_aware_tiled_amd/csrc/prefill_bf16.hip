@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(
     opaque_sizes();
     const Item cur = make_item(bh, it == 0 ? qb : qb2);
     const int Tq = cur.Tq, Tk = cur.Tk, off = Tk - Tq;
-    const int i0 = cur.i0, q_end = cur.q_end, ntiles = cur.ntiles, jm = cur.jm;
+    const int i0 = cur.i0, ntiles = cur.ntiles, jm = cur.jm;
     const int j_lo = cur.j_lo, j_ul = cur.j_ul;
     const __bf16 *Kh = cur.Kh, *Vh = cur.Vh;
     auto clean = [&](int j) { return j >= j_ul && j < jm; };
