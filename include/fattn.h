@@ -138,6 +138,8 @@ int attn_fwd_plan(int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int
  * causal = 1, plus `window` (keys per row, >= 1; FATTN_ERR_INVALID otherwise). A window of Tk or
  * more hides nothing beyond the causal mask and gives exactly the result of attn_fwd with
  * causal = 1. With Tq == 1 and bf16 the split-K decode path reads only the last `window` keys.
+ * A prefill under a window takes the launch table's configuration for a key length of `window`
+ * (the most keys a row sees), with schedule 2 in place of schedule 4.
  */
 int attn_fwd_window(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                     int Hq, int Hkv, int Tq, int Tk, int d, int window, float scale, int dtype,

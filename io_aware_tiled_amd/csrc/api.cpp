@@ -231,9 +231,16 @@ int forward(const void* Q, const void* K, const void* V, void* O, float* LSE, in
   if (window >= Tk) window = 0;
   // Under a window a decode row reads only the last `window` keys: plan the splits on those.
   const int k0 = (window > 0 && Tq == 1) ? Tk - window : 0;
+  // A windowed prefill row sees at most `window` keys: the table's row for that key length, and
+  // the XCD-grouped order in place of paired blocks (pairing evens out the causal triangle; past
+  // the first `window` rows every query block of a window holds the same work).
+  const bool window_prefill = window > 0 && Tq > 1;
   fattn_cfg_t plan;
-  rc = make_plan(B, Hq, Hkv, Tq, Tk - k0, d, causal, dtype, cfg, &plan);
+  rc = make_plan(B, Hq, Hkv, Tq, window_prefill ? window : Tk - k0, d, causal, dtype, cfg, &plan);
   if (rc != FATTN_OK) return fail(rc, "launch configuration not implemented for this shape");
+  if (window_prefill && plan.kernel == FATTN_KERNEL_PREFILL_MFMA && plan.schedule == 4 &&
+      !(cfg && cfg->schedule))
+    plan.schedule = 2;
   if (noalloc && plan.kernel == FATTN_KERNEL_DECODE_SPLITK) {
     // the partials of every split must fit the static scratch: fewer splits if needed
     const size_t per_split = (size_t)B * Hq * (size_t)(d + 1);
