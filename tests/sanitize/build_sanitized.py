@@ -20,6 +20,8 @@ CSRC = os.path.join(ROOT, "io_aware_tiled_amd", "csrc")
 def build(out_dir: str) -> str:
     os.makedirs(out_dir, exist_ok=True)
     lib = os.path.join(out_dir, "libfattn_sanitized.so")
+    # __HIP_PLATFORM_AMD__ only names the platform for the HIP runtime headers, which a plain host
+    # compiler includes here without hipcc's driver defining it
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fvisibility=hidden",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
            "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
