@@ -407,12 +407,14 @@ extern "C" int attn_fwd_varlen(const void* Q, const void* K, const void* V, void
   pk.cu_k = cu_seqlens_k;
   pk.total_q = total_q;
   pk.total_k = total_k;
-  // tile shape from the table for the longest lengths; the grid order is always 3
+  // tile shape from the table for the longest lengths (under a window, for the window: the most
+  // keys a row sees); the grid order is always 3
   fattn_cfg_t cfg = {};
   cfg.kernel = FATTN_KERNEL_PREFILL_MFMA;
   fattn_cfg_t plan;
-  rc = make_plan(num_seqs, Hq, Hkv, max_seqlen_q > 0 ? max_seqlen_q : 1,
-                 max_seqlen_k > 0 ? max_seqlen_k : 1, d, causal, dtype, &cfg, &plan);
+  const int plan_tk = window > 0 ? window : (max_seqlen_k > 0 ? max_seqlen_k : 1);
+  rc = make_plan(num_seqs, Hq, Hkv, max_seqlen_q > 0 ? max_seqlen_q : 1, plan_tk, d, causal, dtype,
+                 &cfg, &plan);
   if (rc != FATTN_OK) return fail(rc, "launch configuration not implemented for this shape");
   hipError_t e = launch_prefill_varlen_bf16(p, pk, plan.block_kv, plan.waves, 3,
                                             reinterpret_cast<hipStream_t>(stream));
