@@ -246,15 +246,19 @@ def counters_for(kernel_source, key):
 
 # ---- the CPU oracle, timed in child processes (one per measurement) before the GPU is touched
 
-# name -> (config, what is timed, units timed, units in the workload, unit name)
+SMALL_F32 = "f32_causal_b1_h4_t128_d32"
+SMALL_BF16 = "bf16_causal_b4_h16_t1024_d64"
+GQA_LONG = "bf16_gqa_causal_b2_hq32_hkv8_t16384_d128"
+# workload -> (what is timed, units timed, units in the workload, unit name)
 ORACLE_CASES = {
-    "C1": ("f32_causal_b1_h4_t128_d32", "all 4 heads", None, None, "heads"),
-    "C2": ("bf16_causal_b4_h16_t1024_d64", "all 64 heads", None, None, "heads"),
-    "C3": (PREFILL, "all 32 heads", None, None, "heads"),
-    "C4": (DECODE, "sequences 0-7 of 64 (all 64 query heads each)", 8, 64, "sequences"),
-    "C5": ("bf16_gqa_causal_b2_hq32_hkv8_t16384_d128",
-           "query heads 0 and 1 of sequence 0 (kv head 0) of 64 heads", 2, 64, "heads"),
+    SMALL_F32: ("all 4 heads", None, None, "heads"),
+    SMALL_BF16: ("all 64 heads", None, None, "heads"),
+    PREFILL: ("all 32 heads", None, None, "heads"),
+    DECODE: ("sequences 0-7 of 64 (all 64 query heads each)", 8, 64, "sequences"),
+    GQA_LONG: ("query heads 0 and 1 of sequence 0 (kv head 0) of 64 heads", 2, 64, "heads"),
 }
+# the workloads also timed on one core
+ONE_CORE = (SMALL_F32, SMALL_BF16, DECODE)
 # the calls timed after the steps, each on a bounded sample: name -> sample description
 BESIDE_CASES = {
     "sliding_window_prefill": "heads 0-3 of 32 of the W=4096 causal T=8192 d=128 prefill, fp64 "
@@ -292,12 +296,12 @@ def oracle_case(name):
 
     res = {}
     if name in ORACLE_CASES:
-        key, _, timed, total, _ = ORACLE_CASES[name]
-        cfg = inputs.CONFIGS[key]
+        _, timed, total, _ = ORACLE_CASES[name]
+        cfg = inputs.CONFIGS[name]
         bs, hq, hk = range(cfg.B), range(cfg.Hq), range(cfg.Hkv)
-        if name == "C4":
+        if name == DECODE:
             bs = range(timed)
-        elif name == "C5":
+        elif name == GQA_LONG:
             bs, hq, hk = [0], [0, 1], [0]
         Q = _slices(cfg, inputs.Q_ID, bs, hq)
         K = _slices(cfg, inputs.K_ID, bs, hk)
@@ -305,13 +309,13 @@ def oracle_case(name):
         t0 = time.perf_counter()
         oracle.dense_attention(Q, K, V, cfg.causal, cfg.scale)
         el = time.perf_counter() - t0
-        if name == "C4":
+        if name == DECODE:
             work, unit = decode_bytes(len(bs), cfg.Hq, cfg.Hkv, cfg.Tk, cfg.d), "bytes"
         else:
             work = prefill_flops(len(bs), len(hq), cfg.Tq, cfg.Tk, cfg.d, cfg.causal)
             unit = "FLOPs"
-        n = len(bs) if name == "C4" else len(bs) * len(hq)
-        res = {"timed": n, "total": cfg.B if name == "C4" else cfg.B * cfg.Hq}
+        n = len(bs) if name == DECODE else len(bs) * len(hq)
+        res = {"timed": n, "total": cfg.B if name == DECODE else cfg.B * cfg.Hq}
     else:
         cfg = inputs.CONFIGS[PREFILL]
         if name == "sliding_window_prefill":
@@ -374,18 +378,18 @@ def cpu_oracle_leg():
     """The oracle timed per workload (all cores; one core for the three small ones), then on
     samples of the calls timed after the steps. Returns (cpu_baseline, per_config, beside)."""
     per = {}
-    for name, (key, what, timed, total, unit) in ORACLE_CASES.items():
-        print(f"[bench] CPU oracle {name} ({key})", file=sys.stderr, flush=True)
+    for name, (what, timed, total, unit) in ORACLE_CASES.items():
+        print(f"[bench] CPU oracle {name}", file=sys.stderr, flush=True)
         r = _oracle_child(name, False)
         scale = r["total"] / r["timed"]
         rate = r["work"] / r["seconds"]
-        e = {"config": key, "timed": what, "threads": r["threads"], "host_cpus": r["cpus"],
+        e = {"timed": what, "threads": r["threads"], "host_cpus": r["cpus"],
              "seconds": round(r["seconds"], 4),
              "seconds_whole_workload": round(r["seconds"] * scale, 4),
              "extrapolated": scale != 1,
              ("gbs" if r["unit"] == "bytes" else "tflops"):
                  rate / 1e9 if r["unit"] == "bytes" else rate / 1e12}
-        if name in ("C1", "C2", "C4"):
+        if name in ONE_CORE:
             r1 = _oracle_child(name, True)
             e["seconds_one_core"] = round(r1["seconds"], 4)
             e["seconds_one_core_whole_workload"] = round(r1["seconds"] * scale, 4)
@@ -399,14 +403,14 @@ def cpu_oracle_leg():
                         "unit": "GB/s" if r["unit"] == "bytes" else "TFLOP/s",
                         "cores": r["threads"], "kind": "oracle",
                         "sample": f"{what}, {r['seconds']:.2f} s"}
-    c3 = per["C3"]
-    head = {"value": c3["tflops"], "unit": "TFLOP/s", "cores": c3["threads"], "kind": "oracle",
+    pre = per[PREFILL]
+    head = {"value": pre["tflops"], "unit": "TFLOP/s", "cores": pre["threads"], "kind": "oracle",
             "sample": f"the whole causal T=8192 d=128 prefill (32 heads, all 8192 rows each), fp64 "
-                      f"dense with S and P materialised, {c3['seconds']:.2f} s in its own process; "
-                      f"the matrix products use {c3['threads']} BLAS threads, the exponentials and "
+                      f"dense with S and P materialised, {pre['seconds']:.2f} s in its own process; "
+                      f"the matrix products use {pre['threads']} BLAS threads, the exponentials and "
                       f"other elementwise steps one; TFLOP/s with the causal-halved FLOP count of "
                       f"the GPU figure",
-            "seconds": c3["seconds"], "host_cpus": c3["host_cpus"]}
+            "seconds": pre["seconds"], "host_cpus": pre["host_cpus"]}
     return head, per, beside
 
 

@@ -4,7 +4,7 @@
 
 api.cpp (argument checks, planning, workspaces, the exported calls) is compiled with g++ as plain
 host C++ and linked with launch_stubs.cpp in place of the HIP kernels, with hidden visibility
-like the real library. Nothing here runs on a GPU: the ABI tests loaded against this build
+like the real library. Nothing here runs on a GPU: the ABI tests loaded against this library
 exercise only the paths that return before any kernel launch.
 """
 

@@ -1,6 +1,6 @@
 // Stand-ins for libfattn's kernel launchers and device scratch lookup, for the host-only
 // sanitizer build of api.cpp (tests/test_sanitized_abi.py). Every one reports that no device is
-// present; the ABI checks that run against this build never get that far.
+// present; the ABI checks that run against this library never get that far.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
