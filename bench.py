@@ -136,7 +136,8 @@ def probes(torch):
     import ctypes
 
     plib = ctypes.CDLL(PROBE_LIB)
-    plib.probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    plib.probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
     plib.probe_mfma_bf16.restype = ctypes.c_int
     plib.probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                     ctypes.c_int, ctypes.c_void_p]
@@ -145,12 +146,16 @@ def probes(torch):
     out = torch.empty(wgs * 512, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
 
-    def mfma():
-        rc = plib.probe_mfma_bf16(out.data_ptr(), wgs, iters, stream)
-        assert rc == 0, rc
+    def mfma_rate(random):
+        def call():
+            rc = plib.probe_mfma_bf16(out.data_ptr(), wgs, iters, random, stream)
+            assert rc == 0, rc
 
-    t = time_calls(torch, mfma, 3, 5)
-    mfma_tflops = wgs * 8 * 32 * iters * 32768.0 / (min(t) * 1e-3) / 1e12
+        t = time_calls(torch, call, 3, 5)
+        return wgs * 8 * 32 * iters * 32768.0 / (min(t) * 1e-3) / 1e12
+
+    mfma_tflops = mfma_rate(0)
+    mfma_random_tflops = mfma_rate(1)
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     rwgs = 16384
@@ -163,11 +168,15 @@ def probes(torch):
     t = time_calls(torch, read, 20, 10)
     read_gbs = nbytes / (min(t) * 1e-3) / 1e9
     del buf, words, out
-    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "hbm_read_gbs": round(read_gbs, 1),
-            "what": "best of 5 (matrix) and 10 (read) launches: 4 chains of v_mfma_f32_32x32x16_bf16 per wavefront on "
-                    "register operands (2048 x 8 wavefronts); 16-byte nontemporal loads over a "
-                    "4 GiB buffer, one contiguous 256 KiB chunk per workgroup (16384 x 256 "
-                    "threads)"}
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1),
+            "mfma_bf16_random_tflops": round(mfma_random_tflops, 1),
+            "hbm_read_gbs": round(read_gbs, 1),
+            "what": "best of 5 (matrix) and 10 (read) launches: 4 chains of "
+                    "v_mfma_f32_32x32x16_bf16 per wavefront on register operands (2048 x 8 "
+                    "wavefronts), small slowly varying operands, then hashed uniform(-1, 1) "
+                    "operands (the clock under matrix load drops with the operand bits that "
+                    "toggle); 16-byte nontemporal loads over a 4 GiB buffer, one contiguous "
+                    "256 KiB chunk per workgroup (16384 x 256 threads)"}
 
 
 def source_hash(name):
@@ -658,6 +667,8 @@ def main():
         "prefill": {"ms": round(prefill_ms, 4), "tflops": round(tflops, 2),
                     "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
                     "pct_of_probe": round(100 * tflops / pr["mfma_bf16_tflops"], 2),
+                    "pct_of_random_operand_probe":
+                        round(100 * tflops / pr["mfma_bf16_random_tflops"], 2),
                     "flops_per_call": flops, "ms_stats": _r(pst),
                     "ms_steps": [round(x, 4) for x in p_steps]},
         "decode": {"ms": round(decode_ms, 4), "gbs": round(gbs, 1),

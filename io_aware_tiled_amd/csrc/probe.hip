@@ -3,12 +3,15 @@
 // attention kernels' rates can be quoted against what is achievable as well as against the
 // published peaks. Not part of libfattn or of its C ABI.
 //
-//  int probe_mfma_bf16(float* out, int workgroups, int iters, void* stream);
+//  int probe_mfma_bf16(float* out, int workgroups, int iters, int random, void* stream);
 //    Enqueues `workgroups` workgroups of 8 wavefronts on `stream`; every wavefront runs four
 //    independent chains of v_mfma_f32_32x32x16_bf16 (the prefill kernel's instruction, 32768
 //    FLOPs each), 32 * iters of them, on register operands, then writes one float per thread to
 //    `out` (device memory of at least workgroups * 512 floats, owned by the caller).
-//    FLOPs per launch: workgroups * 8 * 32 * iters * 32768.
+//    FLOPs per launch: workgroups * 8 * 32 * iters * 32768. With random = 0 the operands are
+//    small slowly varying values; with random = 1 every element is a hashed uniform(-1, 1)
+//    value, as the attention inputs are. The matrix cores run measurably slower on the second
+//    (the chip's clock under matrix load depends on how many operand bits toggle).
 //  int probe_hbm_read(const void* buf, size_t bytes, unsigned* out, int workgroups, void* stream);
 //    Enqueues `workgroups` workgroups of 256 threads that read the `bytes` bytes at device
 //    pointer `buf` once with 16-byte nontemporal loads (the decode kernel's load form),
@@ -29,12 +32,29 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// uniform(-1, 1) from a 32-bit integer hash (xorshift-multiply mixing)
+__device__ __forceinline__ float hashed_uniform(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return (float)(x & 0xffffu) * (1.0f / 32768.0f) - 1.0f;
+}
+
+template <bool RANDOM>
 __global__ __launch_bounds__(512) void probe_mfma_kernel(float* __restrict__ out, int iters) {
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
   bf16x8 a, b;
+  const uint32_t id = blockIdx.x * blockDim.x + threadIdx.x;
   for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(0.001f * (float)(threadIdx.x + i));
-    b[i] = (__bf16)(0.002f * (float)((int)threadIdx.x - i));
+    if (RANDOM) {
+      a[i] = (__bf16)hashed_uniform(16 * id + i);
+      b[i] = (__bf16)hashed_uniform(16 * id + 8 + i);
+    } else {
+      a[i] = (__bf16)(0.001f * (float)(threadIdx.x + i));
+      b[i] = (__bf16)(0.002f * (float)((int)threadIdx.x - i));
+    }
   }
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
@@ -82,10 +102,15 @@ constexpr int kOk = 0, kInvalid = -1, kLaunch = -3;
 
 #define PROBE_API extern "C" __attribute__((visibility("default")))
 
-PROBE_API int probe_mfma_bf16(float* out, int workgroups, int iters, void* stream) {
-  if (!out || workgroups <= 0 || iters <= 0) return kInvalid;
-  hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)workgroups), dim3(512), 0,
-                     reinterpret_cast<hipStream_t>(stream), out, iters);
+PROBE_API int probe_mfma_bf16(float* out, int workgroups, int iters, int random, void* stream) {
+  if (!out || workgroups <= 0 || iters <= 0 || (random != 0 && random != 1)) return kInvalid;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (random)
+    hipLaunchKernelGGL(probe_mfma_kernel<true>, dim3((unsigned)workgroups), dim3(512), 0, s, out,
+                       iters);
+  else
+    hipLaunchKernelGGL(probe_mfma_kernel<false>, dim3((unsigned)workgroups), dim3(512), 0, s, out,
+                       iters);
   return hipGetLastError() == hipSuccess ? kOk : kLaunch;
 }
 

@@ -168,3 +168,20 @@ def test_python_binding_rejects_cpu_tensors():
         fa.attn_fwd(q, q, q)
     with pytest.raises(TypeError):
         fa.attn_fwd(q.half(), q.half(), q.half())
+
+
+def test_probe_library_rejects_invalid_arguments():
+    # the benchmark's measurement probes live in their own library; invalid arguments are refused
+    # before any HIP call
+    import os
+
+    plib = ctypes.CDLL(os.path.join(os.path.dirname(fa.__file__), "libfattn_probe.so"))
+    plib.probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    plib.probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_void_p]
+    for args in [(None, 1, 1, 0), (P, 0, 1, 0), (P, 1, 0, 0), (P, 1, 1, 2), (P, 1, 1, -1)]:
+        assert plib.probe_mfma_bf16(*args, None) == -1
+    for args in [(None, 16, P, 1), (P, 8, P, 1), (P, 24, P, 1), (P + 4, 16, P, 1),
+                 (P, 16, None, 1), (P, 16, P, 0)]:
+        assert plib.probe_hbm_read(*args, None) == -1
