@@ -444,8 +444,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
 }
 
 // ---- dK, dV: one workgroup per (batch, kv head, block of 32 * NW keys); the loop runs over the
-// query heads of the group and, in each, over the query tiles of BC rows that see a key of the
-// block.
+// query heads of the group and the query tiles of BC rows that see a key of the block (the order
+// is given with the step mapping below).
 // VARLEN: packed batch, as for the dQ kernel; blockIdx covers (sequence, kv head, key block).
 // KLDS: the workgroup's K rows live in LDS and are read as the K^T operand of every tile, instead
 // of K^T in registers. At d = 128 this frees the 32 registers that bring the kernel within 256,
@@ -551,10 +551,15 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   for (int rr = 0; rr < 2; ++rr)
     vab[rr] = (rowbase<D, BC, NW>(8 * rr + 4 * vq + ve) ^ ((2 * vg + (va >> 1)) << 4)) + 8 * (va & 1);
 
-  // Q, dO and (L, D) tiles of step s (query head g*G + s / ntq, query tile t_lo + s % ntq)
+  // Step s takes query tile t_lo + ntq - 1 - s / G of query head g*G + s % G: the tiles run from
+  // the last one down, the heads of the group inner, so that the workgroups of one kv head, whose
+  // first tiles differ under a causal mask, read the same Q and dO tiles at the same time (they
+  // meet in L2) instead of each streaming the group's tiles from its own first tile.
+  auto tile_of = [&](int s) { return t_lo + ntq - 1 - s / G; };
+  // Q, dO and (L, D) tiles of step s
   auto issue = [&](int s, unsigned char* qst, unsigned char* ost, float* lw) {
-    const int hh = g * G + s / ntq;
-    const int q0 = (t_lo + s % ntq) * BC;
+    const int hh = g * G + s % G;
+    const int q0 = tile_of(s) * BC;
     if constexpr (VARLEN) {
       const size_t head = (size_t)q_begin * Hq + hh;
       dma_tile_strided<D, BC, NW>(Q + head * D, q0, Tq, (int)qstr, qst, wave, dvo);
@@ -634,7 +639,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void bwd_dkdv_kernel(
   };
 
   auto compute = [&](int s, const unsigned char* qst, const unsigned char* ost, const float* lw) {
-    const int q0 = (t_lo + s % ntq) * BC;
+    const int q0 = tile_of(s) * BC;
     if (kw0 >= Tk || (causal && q0 + BC - 1 + off < kw0) ||
         (window > 0 && q0 + off - window + 1 > kw0 + 31))
       return;  // no row of the tile sees a key of this wave
