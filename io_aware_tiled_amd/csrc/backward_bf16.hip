@@ -7,15 +7,16 @@
 // stored T x T matrix, and with D_i = rowsum(dO o O)_i:
 //   dV = P^T dO,   dP = dO V^T,   dS = P o (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
 //
-// Three kernels, none with atomics, so every result is bitwise reproducible run to run:
-//  * bwd_prep_kernel: D_i and L_i * log2(e) per query row, written in 32-row blocks
-//    [L (32 floats), D (32 floats)]; rows past Tq hold L = +inf and D = 0, so their recomputed
-//    probabilities are exactly 0.
-//  * bwd_dq_kernel (query-block outer loop, like the forward): a lane owns a query row and
-//    streams the K and V tiles of its head; per tile S^T and dP^T come from two MFMA products
-//    against Q^T and dO^T held in registers, dS is formed on the VALU, and dQ^T += K^T dS^T
-//    reads the same K tile transposed. Software-pipelined like the forward: the products of the
-//    next tile are issued together with the current tile's exponentials.
+// Two kernels, none with atomics, so every result is bitwise reproducible run to run:
+//  * bwd_dq_kernel (query-block outer loop, like the forward): a lane owns a query row. It first
+//    forms its row's D_i and L_i * log2(e) and writes them to the workspace for the second
+//    kernel, in 32-row blocks [L (32 floats), D (32 floats)] with rows past Tq holding L = +inf
+//    and D = 0 (so their recomputed probabilities are exactly 0); packed batches use
+//    [Hq, total_q] planes. It then streams the K and V tiles of its head; per tile S^T and dP^T
+//    come from two MFMA products against Q^T and dO^T held in registers, dS is formed on the
+//    VALU, and dQ^T += K^T dS^T reads the same K tile transposed. Software-pipelined like the
+//    forward: the products of the next tile are issued together with the current tile's
+//    exponentials.
 //  * bwd_dkdv_kernel (key-block outer loop): a lane owns a key and holds V^T in registers; at
 //    d = 128 the workgroup's K rows sit in LDS for its whole life (read as the K^T operand), which
 //    keeps the kernel within 256 registers and so at two waves per SIMD (K^T stays in registers
@@ -45,73 +46,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2eF = 1.44269504088896340736f;
 constexpr float kPosInf = __builtin_inff();
-
-// ---- D_i = sum_d dO[i, d] * O[i, d] and L_i * log2(e), per 32-row block of every head.
-// D / 8 lanes read a row (16 bytes each) and reduce across themselves.
-// Packed batches: one row per (query head, token) of [total_q, Hq, D] tensors; L and D are
-// written to ws[h * total_q + token] and ws[Hq * total_q + h * total_q + token] (no padding rows:
-// the gradient kernels mask rows outside a sequence).
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_packed_kernel(const __bf16* __restrict__ O,
-                                                              const __bf16* __restrict__ dO,
-                                                              const float* __restrict__ LSE,
-                                                              float* __restrict__ ws, int Hq,
-                                                              int total_q) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
-  const int tid = threadIdx.x;
-  const int sub = tid % LPR;
-  const long long r = (long long)blockIdx.x * RPB + tid / LPR;  // over Hq * total_q rows
-  const bool valid = r < (long long)Hq * total_q;
-  const int h = valid ? (int)(r / total_q) : 0;
-  const int g = valid ? (int)(r - (long long)h * total_q) : 0;
-  float acc = 0.f;
-  if (valid) {
-    const size_t e = ((size_t)g * Hq + h) * D + 8 * sub;
-    const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + e);
-    const bf16x8 gr = *reinterpret_cast<const bf16x8*>(dO + e);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc = fmaf((float)o[k], (float)gr[k], acc);
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (sub == 0 && valid) {
-    ws[r] = LSE[r] * kLog2eF;
-    ws[(size_t)Hq * total_q + r] = acc;
-  }
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const __bf16* __restrict__ O,
-                                                       const __bf16* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       float* __restrict__ ws, int BH, int Tq,
-                                                       int nqt) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
-  const int tid = threadIdx.x;
-  const int sub = tid % LPR;
-  const long long r = (long long)blockIdx.x * RPB + tid / LPR;  // over BH * nqt * 32 rows
-  const int rows_per_head = nqt * 32;
-  const int bh = (int)(r / rows_per_head);
-  const int i = (int)(r - (long long)bh * rows_per_head);
-  const bool valid = bh < BH && i < Tq;
-  float acc = 0.f;
-  if (valid) {
-    const size_t e = ((size_t)bh * Tq + i) * D + 8 * sub;
-    const bf16x8 o = *reinterpret_cast<const bf16x8*>(O + e);
-    const bf16x8 g = *reinterpret_cast<const bf16x8*>(dO + e);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc = fmaf((float)o[k], (float)g[k], acc);
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (sub == 0 && bh < BH) {
-    float* blk = ws + ((size_t)bh * nqt + i / 32) * 64;
-    blk[i % 32] = valid ? LSE[(size_t)bh * Tq + i] * kLog2eF : kPosInf;
-    blk[32 + i % 32] = valid ? acc : 0.f;
-  }
-}
 
 // A wave's 32 gradient rows (lane (col, hf) holds dims 32dt + 8g4 + 4hf .. +3 of row col in
 // acc[dt][4g4 .. 4g4+3], the MFMA accumulator layout), times `mul`, rounded to bf16 and stored as
@@ -159,15 +93,16 @@ __device__ __forceinline__ void store_rows(unsigned char* a0, unsigned char* a1,
 }
 
 // ---- dQ: one workgroup per (batch, query head, block of 32 * NW query rows).
-// VARLEN: packed batch (Q, dO, dQ [total_q, Hq, D], K, V [total_k, Hkv, D], the workspace of
-// bwd_prep_packed_kernel); blockIdx covers (sequence, head, query block) with Tq and Tk the
-// longest lengths, and each workgroup takes its sequence's lengths from the offsets.
+// VARLEN: packed batch (Q, O, dO, dQ [total_q, Hq, D], K, V [total_k, Hkv, D], LSE
+// [Hq, total_q]); blockIdx covers (sequence, head, query block) with Tq and Tk the longest
+// lengths, and each workgroup takes its sequence's lengths from the offsets.
 template <int D, int BC, int NW, bool VARLEN>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dQ, int Hq,
-    int Hkv, int Tq, int Tk, int causal, int window, float scale, float c,
-    const int* __restrict__ cu_q, const int* __restrict__ cu_k, int total_q, int total_k) {
+    const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ ws, __bf16* __restrict__ dQ, int Hq, int Hkv, int Tq, int Tk, int causal,
+    int window, float scale, float c, const int* __restrict__ cu_q, const int* __restrict__ cu_k,
+    int total_q, int total_k) {
   using S = Shape<D, BC, NW>;
   // One array per stage (K rotates through four, V through two; see the pipeline below), so
   // the compiler can tell a direct-to-LDS load into one stage from reads of another.
@@ -246,16 +181,44 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(
     qb8[kk] = __builtin_bit_cast(bf16x8, rq);
     ob8[kk] = __builtin_bit_cast(bf16x8, ro);
   }
+  // L * log2(e) and D = rowsum(dO * O) of this lane's row: this lane holds half of the row's
+  // dims of dO (the other half is in lane ^ 32) and reads the same dims of O. They are written
+  // to the workspace, in the layout the dK/dV kernel that follows on the stream reads (dense:
+  // per 32-row block, 32 L then 32 D, rows past Tq +inf and 0; packed: [Hq, total_q] planes).
   float Lr = kPosInf, Dr = 0.f;
-  if (qrow < Tq) {
+  {
+    const __bf16* Oh = VARLEN ? O + ((size_t)q_begin * Hq + h) * D : O + (size_t)bh * Tq * D;
+    float acc = 0.f;
+    if (qrow < Tq) {
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const bf16x8 o = *reinterpret_cast<const bf16x8*>(Oh + (size_t)qrow * qstr + 16 * kk +
+                                                          8 * hf);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc = fmaf((float)o[k], (float)ob8[kk][k], acc);
+      }
+    }
+    acc += __shfl_xor(acc, 32);
     if constexpr (VARLEN) {
       const size_t r = (size_t)h * total_q + q_begin + qrow;
-      Lr = ws[r];
-      Dr = ws[(size_t)Hq * total_q + r];
+      if (qrow < Tq) {
+        Lr = LSE[r] * kLog2eF;
+        Dr = acc;
+        if (hf == 0) {
+          ws[r] = Lr;
+          ws[(size_t)Hq * total_q + r] = Dr;
+        }
+      }
     } else {
-      const float* blk = ws + ((size_t)bh * nqt + qrow / 32) * 64;
-      Lr = blk[qrow % 32];
-      Dr = blk[32 + qrow % 32];
+      if (qrow < Tq) {
+        Lr = LSE[(size_t)bh * Tq + qrow] * kLog2eF;
+        Dr = acc;
+      }
+      if (hf == 0 && qrow < nqt * 32) {
+        float* blk = ws + ((size_t)bh * nqt + qrow / 32) * 64;
+        blk[qrow % 32] = Lr;
+        blk[32 + qrow % 32] = Dr;
+      }
     }
   }
 
@@ -753,14 +716,15 @@ hipError_t launch_grads(const BwdProblem& p, const Packed* pk, float* ws, float 
   constexpr int DQ_BC = 32;
   const int nqb = (p.Tq + 32 * DQ_NW - 1) / (32 * DQ_NW);
   const dim3 dq_grid((unsigned)(p.B * p.Hq * nqb)), dq_block(64 * DQ_NW);
+  const __bf16* O = static_cast<const __bf16*>(p.O);
   if (pk)
     bwd_dq_kernel<D, DQ_BC, DQ_NW, true><<<dq_grid, dq_block, 0, stream>>>(
-        Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
-        p.window, p.scale, c, cu_q, cu_k, total_q, total_k);
+        Q, K, V, O, dO, p.LSE, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk,
+        p.causal, p.window, p.scale, c, cu_q, cu_k, total_q, total_k);
   else
     bwd_dq_kernel<D, DQ_BC, DQ_NW, false><<<dq_grid, dq_block, 0, stream>>>(
-        Q, K, V, dO, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk, p.causal,
-        p.window, p.scale, c, nullptr, nullptr, 0, 0);
+        Q, K, V, O, dO, p.LSE, ws, static_cast<__bf16*>(p.dQ), p.Hq, p.Hkv, p.Tq, p.Tk,
+        p.causal, p.window, p.scale, c, nullptr, nullptr, 0, 0);
 
   // K in LDS for the dK/dV workgroups of 4 and 8 waves at d = 128 (two waves per SIMD); K^T in
   // registers below (two waves per SIMD already at d <= 64)
@@ -781,24 +745,9 @@ hipError_t launch_grads(const BwdProblem& p, const Packed* pk, float* ws, float 
 
 template <int D>
 hipError_t launch_d(const BwdProblem& p, const Packed* pk, float* ws, hipStream_t stream) {
-  const int BH = p.B * p.Hq;
-  const int nqt = (p.Tq + 31) / 32;
   const float c = p.scale * kLog2eF;
-  const __bf16* dO = static_cast<const __bf16*>(p.dO);
-
-  constexpr int RPB = 256 / (D / 8);
-  if (pk) {
-    const long long rows = (long long)p.Hq * pk->total_q;
-    bwd_prep_packed_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                                stream>>>(static_cast<const __bf16*>(p.O), dO, p.LSE, ws, p.Hq,
-                                          pk->total_q);
-  } else {
-    const long long rows = (long long)BH * nqt * 32;
-    bwd_prep_kernel<D><<<dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream>>>(
-        static_cast<const __bf16*>(p.O), dO, p.LSE, ws, BH, p.Tq, nqt);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // (L, D) of every row are formed by the dQ kernel itself, which writes them to the workspace
+  // for the dK/dV kernel that follows (no separate pass over O and dO).
   // Workgroup size by the keys an average row sees (half the longest sequence when causal, at
   // most the window). Up to 2048: 4-wave dQ workgroups (128 query rows), whose doubled workgroup
   // count balances the CUs better (against 8 waves 16-21% faster on causal d = 64 and 128 at
